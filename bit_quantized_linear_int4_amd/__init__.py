@@ -1,0 +1,239 @@
+"""Python binding of libwq, the MI355X group-wise low-bit quantized linear library.
+
+Argument marshalling only: every function below forwards to the C entry point
+of the same name in ``libwq.so`` (declared in ``include/wq.h``), passing device
+pointers of torch tensors and the current HIP stream.  All computation happens
+in the library's HIP kernels; there is no fallback path.  If ``libwq.so`` has
+not been built, importing works but the first call raises ``WqError``.
+
+Tensors are torch CUDA (HIP) tensors; dtypes map as float16 -> WQ_F16,
+bfloat16 -> WQ_BF16, float32 -> WQ_F32.  Outputs are caller-allocated (the
+``alloc_*`` helpers allocate the documented shapes).
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "WqError", "QuantizedWeight", "F16", "BF16", "F32",
+    "FMT_INT4_ASYM", "FMT_NF4", "FMT_INT8_SYM_ROW",
+    "wq_quantize_groupwise", "wq_pack_nf4", "wq_nf4_codebook",
+    "wq_linear_w4a16_workspace", "wq_linear_w4a16",
+    "wq_int8_prepare_activations", "wq_linear_int8_decomp_workspace",
+    "wq_linear_int8_decomp", "wq_dequantize", "wq_status_string",
+    "alloc_int4", "alloc_nf4", "alloc_int8", "library_path",
+]
+
+F16, BF16, F32 = 0, 1, 2
+FMT_INT4_ASYM, FMT_NF4, FMT_INT8_SYM_ROW = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libwq.so")
+_lib = None
+
+
+class WqError(RuntimeError):
+    """A libwq call returned a non-zero wq_status (or the library is missing)."""
+
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("zeros", ctypes.c_void_p), ("scales2", ctypes.c_void_p),
+        ("group2", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise WqError(-1, f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                          "or python -m bit_quantized_linear_int4_amd._build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    c_i32, c_i64, c_vp, c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    wp = ctypes.POINTER(_Weight)
+    sig = {
+        "wq_quantize_groupwise": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                          c_vp, c_vp, c_vp, c_vp]),
+        "wq_pack_nf4": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                c_vp, c_vp, c_vp, c_vp]),
+        "wq_nf4_codebook": (c_i32, [ctypes.POINTER(ctypes.c_float)]),
+        "wq_linear_w4a16_workspace": (ctypes.c_size_t, [c_i64, wp]),
+        "wq_linear_w4a16": (c_i32, [c_vp, c_i32, c_i64, wp, c_vp, c_i32, c_vp,
+                                    ctypes.c_size_t, c_vp]),
+        "wq_int8_prepare_activations": (c_i32, [c_vp, c_i64, c_i64, c_f, c_vp, c_vp, c_vp,
+                                                c_vp, c_vp, c_vp]),
+        "wq_linear_int8_decomp_workspace": (ctypes.c_size_t, [c_i64, c_i64]),
+        "wq_linear_int8_decomp": (c_i32, [c_vp, c_i64, wp, c_f, c_vp, c_i32, c_vp,
+                                          ctypes.c_size_t, c_vp, c_vp, c_vp]),
+        "wq_dequantize": (c_i32, [wp, c_vp, c_i32, c_vp]),
+        "wq_status_string": (ctypes.c_char_p, [c_i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def wq_status_string(status):
+    return _load().wq_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise WqError(status, f"{what}: {wq_status_string(status)}")
+
+
+def _dt(t):
+    import torch
+    m = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    if t.dtype not in m:
+        raise WqError(4, f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, t):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class QuantizedWeight:
+    """Device tensors of one quantized weight plus its wq_weight descriptor."""
+
+    def __init__(self, fmt, n, k, group, codes, scales, zeros=None, scales2=None, group2=0):
+        self.fmt, self.n, self.k, self.group = fmt, int(n), int(k), int(group)
+        self.codes, self.scales, self.zeros, self.scales2 = codes, scales, zeros, scales2
+        self.group2 = int(group2)
+
+    def descriptor(self):
+        d = _Weight()
+        d.fmt, d.group, d.n, d.k = self.fmt, self.group, self.n, self.k
+        d.codes = self.codes.data_ptr()
+        d.scales = self.scales.data_ptr()
+        d.zeros = self.zeros.data_ptr() if self.zeros is not None else None
+        d.scales2 = self.scales2.data_ptr() if self.scales2 is not None else None
+        d.group2 = self.group2
+        d.reserved = 0
+        return d
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size()
+                   for t in (self.codes, self.scales, self.zeros, self.scales2) if t is not None)
+
+    def clone(self):
+        c = lambda t: None if t is None else t.clone()
+        return QuantizedWeight(self.fmt, self.n, self.k, self.group, c(self.codes),
+                               c(self.scales), c(self.zeros), c(self.scales2), self.group2)
+
+
+def alloc_int4(n, k, group=128, device="cuda"):
+    import torch
+    g = k // group
+    return QuantizedWeight(
+        FMT_INT4_ASYM, n, k, group,
+        torch.empty((n, k // 8), dtype=torch.int32, device=device),
+        torch.empty((n, g), dtype=torch.float16, device=device),
+        torch.empty((n, (g + 1) // 2), dtype=torch.uint8, device=device))
+
+
+def alloc_nf4(n, k, block=64, double_quant=True, block2=256, device="cuda"):
+    import torch
+    nb = n * k // block
+    codes = torch.empty((n * k // 2,), dtype=torch.uint8, device=device)
+    if double_quant:
+        return QuantizedWeight(FMT_NF4, n, k, block, codes,
+                               torch.empty((nb,), dtype=torch.int8, device=device),
+                               None, torch.empty(((nb + block2 - 1) // block2,),
+                                                 dtype=torch.float32, device=device), block2)
+    return QuantizedWeight(FMT_NF4, n, k, block, codes,
+                           torch.empty((nb,), dtype=torch.float32, device=device))
+
+
+def alloc_int8(n, k, device="cuda"):
+    import torch
+    return QuantizedWeight(FMT_INT8_SYM_ROW, n, k, k,
+                           torch.empty((n, k), dtype=torch.int8, device=device),
+                           torch.empty((n,), dtype=torch.float32, device=device))
+
+
+def wq_quantize_groupwise(w, bits, group, symmetric, codes, scales, zeros=None, stream=None):
+    n, k = w.shape
+    st = _load().wq_quantize_groupwise(_ptr(w), _dt(w), n, k, bits, group, symmetric,
+                                       _ptr(codes), _ptr(scales), _ptr(zeros), _stream(stream, w))
+    _check(st, "wq_quantize_groupwise")
+
+
+def wq_pack_nf4(w, block, double_quant, block2, codes, absmax, absmax_scale=None, stream=None):
+    n, k = w.shape
+    st = _load().wq_pack_nf4(_ptr(w), _dt(w), n, k, block, 1 if double_quant else 0, block2,
+                             _ptr(codes), _ptr(absmax), _ptr(absmax_scale), _stream(stream, w))
+    _check(st, "wq_pack_nf4")
+
+
+def wq_nf4_codebook():
+    out = (ctypes.c_float * 16)()
+    _check(_load().wq_nf4_codebook(out), "wq_nf4_codebook")
+    return [float(v) for v in out]
+
+
+def wq_linear_w4a16_workspace(m, weight):
+    d = weight.descriptor()
+    return int(_load().wq_linear_w4a16_workspace(int(m), ctypes.byref(d)))
+
+
+def wq_linear_w4a16(x, weight, y, workspace=None, stream=None):
+    d = weight.descriptor()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().wq_linear_w4a16(_ptr(x), _dt(x), x.shape[0], ctypes.byref(d), _ptr(y), _dt(y),
+                                 _ptr(workspace), ws_bytes, _stream(stream, x))
+    _check(st, "wq_linear_w4a16")
+
+
+def wq_int8_prepare_activations(x, threshold, mask, idx, count, qx, sx, stream=None):
+    m, k = x.shape
+    st = _load().wq_int8_prepare_activations(_ptr(x), m, k, float(threshold), _ptr(mask),
+                                             _ptr(idx), _ptr(count), _ptr(qx), _ptr(sx),
+                                             _stream(stream, x))
+    _check(st, "wq_int8_prepare_activations")
+
+
+def wq_linear_int8_decomp_workspace(m, k):
+    return int(_load().wq_linear_int8_decomp_workspace(int(m), int(k)))
+
+
+def wq_linear_int8_decomp(x, weight, threshold, y, workspace, outlier_count=None, acc_out=None,
+                          stream=None):
+    d = weight.descriptor()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().wq_linear_int8_decomp(_ptr(x), x.shape[0], ctypes.byref(d), float(threshold),
+                                       _ptr(y), _dt(y), _ptr(workspace), ws_bytes,
+                                       _ptr(outlier_count), _ptr(acc_out), _stream(stream, x))
+    _check(st, "wq_linear_int8_decomp")
+
+
+def wq_dequantize(weight, out, stream=None):
+    d = weight.descriptor()
+    st = _load().wq_dequantize(ctypes.byref(d), _ptr(out), _dt(out), _stream(stream, out))
+    _check(st, "wq_dequantize")

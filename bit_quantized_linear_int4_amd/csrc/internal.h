@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP translation units of libwq.
+// Not part of the public ABI (that is include/wq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "wq.h"
+
+namespace wq {
+
+// ---------------------------------------------------------------- vectors
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int uint4_t __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------- 16-bit <-> fp32 helpers
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  _Float16 h = (_Float16)v;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+template <int DT>
+__device__ __forceinline__ float load16(const uint16_t* p) {
+  return DT == WQ_BF16 ? bf16_bits_to_f32(*p) : f16_bits_to_f32(*p);
+}
+
+// ------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; shapes were validated by the
+// ABI layer.
+hipError_t launch_quant_int4(const void* w, int wdt, int64_t n, int64_t k, int group,
+                             uint32_t* codes, uint16_t* scales, uint8_t* zeros,
+                             hipStream_t s);
+hipError_t launch_quant_int8_rows(const void* w, int wdt, int64_t n, int64_t k,
+                                  int8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_pack_nf4(const void* w, int wdt, int64_t numel, int double_quant,
+                           const float* thresholds15, uint8_t* codes, void* absmax,
+                           float* absmax_scale, hipStream_t s);
+
+struct W4Plan {
+  int path;      // 0 = decode kernel (m <= 16), 1 = gemm
+  int tpg;       // row tiles of 16 per workgroup (decode)
+  int gpw;       // groups of 128 per wave (decode); a workgroup covers 4*gpw
+  int mp;        // activation rows staged in LDS: 1, 4 or 16 (decode)
+  int splits;    // K chunks across workgroups (decode)
+  size_t ws;     // workspace bytes (fp32 partial sums when splits > 1)
+};
+W4Plan plan_w4a16(int64_t m, const wq_weight* w);
+hipError_t launch_w4a16(const void* x, int xdt, int64_t m, const wq_weight* w,
+                        const float* levels16, void* y, int ydt, void* ws,
+                        const W4Plan& plan, hipStream_t s);
+
+hipError_t launch_int8_prepare(const uint16_t* x, int64_t m, int64_t k, float thr,
+                               uint8_t* mask, int32_t* idx, int32_t* count, int8_t* qx,
+                               float* sx, hipStream_t s);
+hipError_t launch_int8_gemm(const uint16_t* x, int64_t m, const wq_weight* w,
+                            const int8_t* qx, const float* sx, const int32_t* idx,
+                            const int32_t* count, void* y, int ydt, int32_t* acc_out,
+                            hipStream_t s);
+
+hipError_t launch_dequantize(const wq_weight* w, const float* levels16, void* out, int odt,
+                             hipStream_t s);
+
+// Host-side NF4 codebook (levels) and decision midpoints (thresholds).
+const float* nf4_levels();
+const float* nf4_thresholds();
+
+}  // namespace wq

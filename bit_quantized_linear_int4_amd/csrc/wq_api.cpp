@@ -1,0 +1,222 @@
+// C ABI of libwq: argument validation, schedule choice, launch.
+//
+// Every check runs before the first HIP call, so an error other than
+// WQ_ERR_HIP means nothing was enqueued.  No C++ exception crosses the ABI.
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+using namespace wq;
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 38;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool is16(int32_t dt) { return dt == WQ_F16 || dt == WQ_BF16; }
+bool is_out(int32_t dt) { return dt == WQ_F16 || dt == WQ_BF16 || dt == WQ_F32; }
+uintptr_t dt_bytes(int32_t dt) { return dt == WQ_F32 ? 4 : 2; }
+
+wq_status hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_HIP; }
+
+bool sizes_ok(int64_t n, int64_t k) {
+  return n >= 1 && k >= 1 && n < (int64_t(1) << 31) && k < (int64_t(1) << 31) &&
+         n <= kMaxElems / k;
+}
+
+// Validates a weight descriptor for the given use.  `linear_w4` restricts to
+// the formats and group sizes wq_linear_w4a16 runs.
+wq_status check_weight(const wq_weight* w, bool linear_w4) {
+  if (w == nullptr || w->codes == nullptr || w->scales == nullptr) return WQ_ERR_NULL;
+  if (!sizes_ok(w->n, w->k)) return WQ_ERR_SHAPE;
+  if (!aligned(w->codes, 16)) return WQ_ERR_ALIGN;
+  switch (w->fmt) {
+    case WQ_FMT_INT4_ASYM:
+      if (w->zeros == nullptr) return WQ_ERR_NULL;
+      if (w->group != 32 && w->group != 64 && w->group != 128) return WQ_ERR_UNSUPPORTED;
+      if (w->k % w->group != 0 || w->k % 8 != 0) return WQ_ERR_SHAPE;
+      if (!aligned(w->scales, 2)) return WQ_ERR_ALIGN;
+      if (linear_w4 && w->group != 128) return WQ_ERR_UNSUPPORTED;
+      return WQ_OK;
+    case WQ_FMT_NF4:
+      if (w->group != 64) return WQ_ERR_UNSUPPORTED;
+      if (w->scales2 != nullptr && w->group2 != 256) return WQ_ERR_UNSUPPORTED;
+      if ((w->n * w->k) % 64 != 0 || w->k % 8 != 0) return WQ_ERR_SHAPE;
+      if (w->scales2 == nullptr && !aligned(w->scales, 4)) return WQ_ERR_ALIGN;
+      if (w->scales2 != nullptr && !aligned(w->scales2, 4)) return WQ_ERR_ALIGN;
+      return WQ_OK;
+    case WQ_FMT_INT8_SYM_ROW:
+      if (linear_w4) return WQ_ERR_UNSUPPORTED;
+      if (w->group != w->k || w->k % 16 != 0) return WQ_ERR_SHAPE;
+      if (!aligned(w->scales, 4)) return WQ_ERR_ALIGN;
+      return WQ_OK;
+    default:
+      return WQ_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wq_status_string(int32_t status) {
+  switch (status) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_ERR_NULL: return "WQ_ERR_NULL: a required pointer is NULL";
+    case WQ_ERR_SHAPE: return "WQ_ERR_SHAPE: sizes do not fit the format";
+    case WQ_ERR_ALIGN: return "WQ_ERR_ALIGN: a pointer misses its alignment";
+    case WQ_ERR_UNSUPPORTED: return "WQ_ERR_UNSUPPORTED: combination not implemented";
+    case WQ_ERR_WORKSPACE: return "WQ_ERR_WORKSPACE: workspace missing or too small";
+    case WQ_ERR_HIP: return "WQ_ERR_HIP: kernel launch failed";
+    default: return "unknown wq_status";
+  }
+}
+
+wq_status wq_nf4_codebook(float* out) {
+  if (out == nullptr) return WQ_ERR_NULL;
+  const float* l = nf4_levels();
+  for (int i = 0; i < 16; ++i) out[i] = l[i];
+  return WQ_OK;
+}
+
+wq_status wq_quantize_groupwise(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t bits,
+                                int32_t group, int32_t symmetric, void* codes, void* scales,
+                                uint8_t* zeros, void* stream) {
+  if (w == nullptr || codes == nullptr || scales == nullptr) return WQ_ERR_NULL;
+  if (!is16(wdt)) return WQ_ERR_UNSUPPORTED;
+  if (!sizes_ok(n, k) || k % 8 != 0) return WQ_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(codes, 16)) return WQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bits == 4 && symmetric == 0) {
+    if (zeros == nullptr) return WQ_ERR_NULL;
+    if (group != 32 && group != 64 && group != 128) return WQ_ERR_UNSUPPORTED;
+    if (k % group != 0) return WQ_ERR_SHAPE;
+    if (!aligned(scales, 2)) return WQ_ERR_ALIGN;
+    return hip_status(launch_quant_int4(w, wdt, n, k, group, static_cast<uint32_t*>(codes),
+                                        static_cast<uint16_t*>(scales), zeros, s));
+  }
+  if (bits == 8 && symmetric == 1) {
+    if (group != k) return WQ_ERR_UNSUPPORTED;
+    if (zeros != nullptr) return WQ_ERR_UNSUPPORTED;
+    if (!aligned(scales, 4)) return WQ_ERR_ALIGN;
+    return hip_status(launch_quant_int8_rows(w, wdt, n, k, static_cast<int8_t*>(codes),
+                                             static_cast<float*>(scales), s));
+  }
+  return WQ_ERR_UNSUPPORTED;
+}
+
+wq_status wq_pack_nf4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t block,
+                      int32_t double_quant, int32_t block2, uint8_t* codes, void* absmax,
+                      float* absmax_scale, void* stream) {
+  if (w == nullptr || codes == nullptr || absmax == nullptr) return WQ_ERR_NULL;
+  if (!is16(wdt)) return WQ_ERR_UNSUPPORTED;
+  if (block != 64) return WQ_ERR_UNSUPPORTED;
+  if (double_quant) {
+    if (absmax_scale == nullptr) return WQ_ERR_NULL;
+    if (block2 != 256) return WQ_ERR_UNSUPPORTED;
+    if (!aligned(absmax_scale, 4)) return WQ_ERR_ALIGN;
+  } else {
+    if (absmax_scale != nullptr) return WQ_ERR_UNSUPPORTED;
+    if (!aligned(absmax, 4)) return WQ_ERR_ALIGN;
+  }
+  if (!sizes_ok(n, k) || (n * k) % 64 != 0) return WQ_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(codes, 16)) return WQ_ERR_ALIGN;
+  return hip_status(launch_pack_nf4(w, wdt, n * k, double_quant ? 1 : 0, nf4_thresholds(), codes,
+                                    absmax, absmax_scale, static_cast<hipStream_t>(stream)));
+}
+
+size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w) {
+  if (m < 1 || m >= (int64_t(1) << 31) || check_weight(w, true) != WQ_OK) return 0;
+  return plan_w4a16(m, w).ws;
+}
+
+wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight* w, void* y,
+                          int32_t ydt, void* workspace, size_t ws_bytes, void* stream) {
+  if (x == nullptr || y == nullptr) return WQ_ERR_NULL;
+  const wq_status ws = check_weight(w, true);
+  if (ws != WQ_OK) return ws;
+  if (!is16(xdt) || !is_out(ydt)) return WQ_ERR_UNSUPPORTED;
+  if (m < 1 || m >= (int64_t(1) << 31) || m > kMaxElems / w->k || m > kMaxElems / w->n)
+    return WQ_ERR_SHAPE;
+  if (w->k % 128 != 0) return WQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;
+  const W4Plan plan = plan_w4a16(m, w);
+  if (plan.ws > 0) {
+    if (workspace == nullptr || ws_bytes < plan.ws) return WQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return WQ_ERR_ALIGN;
+  }
+  return hip_status(launch_w4a16(x, xdt, m, w, nf4_levels(), y, ydt, workspace, plan,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t wq_linear_int8_decomp_workspace(int64_t m, int64_t k) {
+  if (m < 1 || k < 16 || k % 16 != 0 || !sizes_ok(m, k)) return 0;
+  // mask u8[k] | idx i32[k] | count i32 | qx i8[m][k] | sx f32[m], each 256-aligned
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  return up((size_t)k) + up(4 * (size_t)k) + up(4) + up((size_t)m * (size_t)k) + up(4 * (size_t)m);
+}
+
+wq_status wq_int8_prepare_activations(const void* x, int64_t m, int64_t k, float threshold,
+                                      uint8_t* mask, int32_t* idx, int32_t* count, int8_t* qx,
+                                      float* sx, void* stream) {
+  if (x == nullptr || mask == nullptr || idx == nullptr || count == nullptr || qx == nullptr ||
+      sx == nullptr)
+    return WQ_ERR_NULL;
+  if (!sizes_ok(m, k) || k % 16 != 0) return WQ_ERR_SHAPE;
+  if (!(threshold >= 0.0f)) return WQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
+      !aligned(sx, 4))
+    return WQ_ERR_ALIGN;
+  return hip_status(launch_int8_prepare(static_cast<const uint16_t*>(x), m, k, threshold, mask,
+                                        idx, count, qx, sx, static_cast<hipStream_t>(stream)));
+}
+
+wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w, float threshold,
+                                void* y, int32_t ydt, void* workspace, size_t ws_bytes,
+                                int32_t* outlier_count, int32_t* acc_out, void* stream) {
+  if (x == nullptr || y == nullptr) return WQ_ERR_NULL;
+  const wq_status st = check_weight(w, false);
+  if (st != WQ_OK) return st;
+  if (w->fmt != WQ_FMT_INT8_SYM_ROW) return WQ_ERR_UNSUPPORTED;
+  if (ydt != WQ_F16 && ydt != WQ_F32) return WQ_ERR_UNSUPPORTED;
+  if (!sizes_ok(m, w->k) || m > kMaxElems / w->n || w->k % 128 != 0) return WQ_ERR_SHAPE;
+  if (!(threshold >= 0.0f)) return WQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;
+  if (outlier_count != nullptr && !aligned(outlier_count, 4)) return WQ_ERR_ALIGN;
+  if (acc_out != nullptr && !aligned(acc_out, 4)) return WQ_ERR_ALIGN;
+  const size_t need = wq_linear_int8_decomp_workspace(m, w->k);
+  if (workspace == nullptr || ws_bytes < need) return WQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
+  auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
+  const size_t k = (size_t)w->k;
+  char* base = static_cast<char*>(workspace);
+  uint8_t* mask = reinterpret_cast<uint8_t*>(base);
+  int32_t* idx = reinterpret_cast<int32_t*>(base + up(k));
+  int32_t* count = reinterpret_cast<int32_t*>(base + up(k) + up(4 * k));
+  int8_t* qx = reinterpret_cast<int8_t*>(base + up(k) + up(4 * k) + up(4));
+  float* sx = reinterpret_cast<float*>(base + up(k) + up(4 * k) + up(4) + up((size_t)m * k));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  hipError_t e = launch_int8_prepare(xp, m, w->k, threshold, mask, idx, count, qx, sx, s);
+  if (e != hipSuccess) return WQ_ERR_HIP;
+  e = launch_int8_gemm(xp, m, w, qx, sx, idx, count, y, ydt, acc_out, s);
+  if (e != hipSuccess) return WQ_ERR_HIP;
+  if (outlier_count != nullptr) {
+    e = hipMemcpyAsync(outlier_count, count, sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return WQ_ERR_HIP;
+  }
+  return WQ_OK;
+}
+
+wq_status wq_dequantize(const wq_weight* w, void* out, int32_t odt, void* stream) {
+  if (out == nullptr) return WQ_ERR_NULL;
+  const wq_status st = check_weight(w, false);
+  if (st != WQ_OK) return st;
+  if (!is16(odt)) return WQ_ERR_UNSUPPORTED;
+  if (!aligned(out, 16)) return WQ_ERR_ALIGN;
+  return hip_status(
+      launch_dequantize(w, nf4_levels(), out, odt, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, reports its codebook, and rejects bad arguments before any
+HIP call (the header promises that an error other than WQ_ERR_HIP enqueued
+nothing, so these calls never reach the device)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_linear_int4_amd as wq
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(wq.library_path()),
+                                reason="libwq.so not built")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_documented_surface():
+    names = declared_functions()
+    for required in ("wq_quantize_groupwise", "wq_pack_nf4", "wq_linear_w4a16",
+                     "wq_linear_int8_decomp"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(wq.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(7):
+        assert wq.wq_status_string(s).startswith("WQ_")
+    assert "unknown" in wq.wq_status_string(99)
+
+
+def test_library_codebook_matches_oracle():
+    """The library derives the NF4 levels with its own quantile routine;
+    they must equal the oracle's in fp32."""
+    lib_levels = np.array(wq.wq_nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_levels, nf4.codebook())
+
+
+# fake device addresses: never dereferenced, because validation fails first
+A16 = 0x10000
+ODD = 0x10001
+
+
+def _lib():
+    return wq._load()
+
+
+def test_quantize_argument_errors():
+    q = _lib().wq_quantize_groupwise
+    args = dict(w=A16, wdt=wq.F16, n=4, k=256, bits=4, group=128, sym=0,
+                codes=A16, scales=A16, zeros=A16)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return q(a["w"], a["wdt"], a["n"], a["k"], a["bits"], a["group"], a["sym"],
+                 a["codes"], a["scales"], a["zeros"], None)
+
+    assert call(w=None) == NULL
+    assert call(zeros=None) == NULL
+    assert call(k=100) == SHAPE
+    assert call(k=192) == SHAPE            # not a multiple of the group
+    assert call(n=0) == SHAPE
+    assert call(n=-3) == SHAPE
+    assert call(w=ODD) == ALIGN
+    assert call(codes=A16 + 4) == ALIGN
+    assert call(group=96) == UNSUP
+    assert call(bits=3) == UNSUP
+    assert call(wdt=wq.F32) == UNSUP
+    assert call(bits=8, sym=1, group=256, zeros=None, scales=A16 + 2) == ALIGN
+    assert call(bits=8, sym=1, group=128, zeros=None) == UNSUP
+    assert call(bits=8, sym=1, group=256) == UNSUP  # zeros must be NULL
+
+
+def test_pack_nf4_argument_errors():
+    p = _lib().wq_pack_nf4
+
+    def call(w=A16, wdt=wq.BF16, n=4, k=256, block=64, dq=1, block2=256, codes=A16,
+             absmax=A16, scale2=A16):
+        return p(w, wdt, n, k, block, dq, block2, codes, absmax, scale2, None)
+
+    assert call(codes=None) == NULL
+    assert call(scale2=None) == NULL
+    assert call(block=32) == UNSUP
+    assert call(block2=128) == UNSUP
+    assert call(dq=0) == UNSUP              # second-level scale given without double quant
+    assert call(n=1, k=40) == SHAPE
+    assert call(w=ODD) == ALIGN
+
+
+def _weight(fmt=wq.FMT_INT4_ASYM, n=64, k=256, group=128, codes=A16, scales=A16, zeros=A16,
+            scales2=None, group2=0):
+    d = wq._Weight()
+    d.fmt, d.group, d.n, d.k = fmt, group, n, k
+    d.codes, d.scales, d.zeros, d.scales2 = codes, scales, zeros, scales2
+    d.group2 = group2
+    return d
+
+
+def test_linear_w4a16_argument_errors():
+    f = _lib().wq_linear_w4a16
+
+    def call(x=A16, xdt=wq.F16, m=1, w=None, y=A16, ydt=wq.F32, ws=None, wsb=0):
+        w = _weight() if w is None else w
+        return f(x, xdt, m, ctypes.byref(w), y, ydt, ws, wsb, None)
+
+    assert call(x=None) == NULL
+    assert call(w=_weight(codes=None)) == NULL
+    assert call(w=_weight(zeros=None)) == NULL
+    assert call(m=0) == SHAPE
+    assert call(w=_weight(k=200, group=8)) == UNSUP
+    assert call(w=_weight(group=64)) == UNSUP     # linear runs group 128
+    assert call(w=_weight(k=136)) == SHAPE
+    assert call(x=ODD) == ALIGN
+    assert call(w=_weight(codes=A16 + 8)) == ALIGN
+    assert call(xdt=wq.F32) == UNSUP
+    assert call(ydt=7) == UNSUP
+    assert call(w=_weight(fmt=wq.FMT_INT8_SYM_ROW, group=256)) == UNSUP
+    assert call(w=_weight(fmt=wq.FMT_NF4, group=64, zeros=None, scales2=A16, group2=128)) == UNSUP
+    # a split-K schedule needs scratch: a missing workspace is reported
+    big = _weight(n=4096, k=11008)
+    need = _lib().wq_linear_w4a16_workspace(16, ctypes.byref(big))
+    assert need > 0
+    assert call(w=big, m=16) == WS
+    assert call(w=big, m=16, ws=A16, wsb=need - 1) == WS
+
+
+def test_workspace_queries():
+    lib = _lib()
+    d = _weight(n=4096, k=11008)
+    assert lib.wq_linear_w4a16_workspace(0, ctypes.byref(d)) == 0
+    assert lib.wq_linear_w4a16_workspace(2048, ctypes.byref(d)) == 0   # GEMM path: none
+    assert lib.wq_linear_int8_decomp_workspace(256, 8192) >= 256 * 8192 + 8192 * 5
+    assert lib.wq_linear_int8_decomp_workspace(0, 8192) == 0
+
+
+def test_int8_argument_errors():
+    f = _lib().wq_linear_int8_decomp
+    w = _weight(fmt=wq.FMT_INT8_SYM_ROW, n=64, k=256, group=256, zeros=None)
+    need = _lib().wq_linear_int8_decomp_workspace(4, 256)
+
+    def call(x=A16, m=4, w=w, thr=6.0, y=A16, ydt=wq.F16, ws=A16, wsb=None):
+        return f(x, m, ctypes.byref(w), thr, y, ydt, ws, need if wsb is None else wsb,
+                 None, None, None)
+
+    assert call(x=None) == NULL
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ydt=wq.BF16) == UNSUP
+    assert call(thr=-1.0) == SHAPE
+    assert call(thr=float("nan")) == SHAPE
+    assert call(ws=A16 + 16) == ALIGN
+    w2 = _weight(fmt=wq.FMT_INT8_SYM_ROW, n=64, k=200, group=200, zeros=None)
+    assert call(w=w2) == SHAPE
+    p = _lib().wq_int8_prepare_activations
+    assert p(A16, 4, 256, 6.0, A16, A16, A16, None, A16, None) == NULL
+    assert p(A16, 4, 250, 6.0, A16, A16, A16, A16, A16, None) == SHAPE
+
+
+def test_dequantize_argument_errors():
+    f = _lib().wq_dequantize
+    assert f(ctypes.byref(_weight()), None, wq.F16, None) == NULL
+    assert f(ctypes.byref(_weight()), A16, wq.F32, None) == UNSUP
+    assert f(ctypes.byref(_weight()), ODD, wq.F16, None) == ALIGN
+    assert f(None, A16, wq.F16, None) == NULL

@@ -1,0 +1,118 @@
+"""GPU parity of the NF4 path (blockwise absmax, double quantization, bf16
+compute) against the CPU oracle, through the C ABI.
+
+Codes, first-level int8 absmax codes and second-level scales are bit-exact;
+the dequantized weights are bit-exact; float outputs are judged on fp32
+output (a bf16 output's own rounding is close to the 2e-3 budget) and, for
+bf16 outputs, with the output rounding added to the bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_linear_int4_amd as wq
+import workloads
+from oracle import linear, nf4
+from gpu_util import check_close, dev, host16, say, to_np, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_pack(w_dev, double_quant=True):
+    n, k = w_dev.shape
+    qw = wq.alloc_nf4(n, k, double_quant=double_quant)
+    wq.wq_pack_nf4(w_dev, 64, double_quant, 256, qw.codes, qw.scales, qw.scales2)
+    return qw
+
+
+@pytest.mark.parametrize("n,k,dtype,dq", [
+    (64, 512, "bf16", True),
+    (37, 640, "bf16", True),       # numel not a multiple of 256 blocks
+    (37, 640, "f16", False),
+    (14336, 4096, "bf16", True),   # the 8B-shaped layer
+])
+def test_pack_nf4_bitexact(n, k, dtype, dq):
+    say(f"pack_nf4 n={n} k={k} dtype={dtype} dq={dq}")
+    w = workloads.weights(n, k, 40 + n, 1, dtype=dtype)
+    if n == 64:
+        wv = host16(w, dtype).copy()
+        wv[0, :64] = 0                      # all-zero block -> code 7
+        wv[1, :64] = np.linspace(-1, 1, 64)  # exact +-absmax present
+        w = workloads.to_bf16_bits(wv) if dtype == "bf16" else wv.astype(np.float16)
+    qw = gpu_pack(dev(w, dtype), dq)
+    torch.cuda.synchronize()
+    ref_codes, ref_a, ref_c2 = nf4.quantize(host16(w, dtype), double_quant=dq)
+    assert np.array_equal(qw.codes.cpu().numpy(), ref_codes)
+    if dq:
+        assert np.array_equal(qw.scales.cpu().numpy(), ref_a)
+        assert np.array_equal(qw.scales2.cpu().numpy(), ref_c2)
+    else:
+        assert np.array_equal(qw.scales.cpu().numpy(), ref_a)
+
+
+@pytest.mark.parametrize("dq,odt", [(True, "bf16"), (False, "bf16"), (True, "f16")])
+def test_dequantize_nf4_bitexact(dq, odt):
+    say(f"dequantize_nf4 dq={dq} odt={odt}")
+    n, k = 40, 1024
+    w = workloads.weights(n, k, 77, 1, dtype="bf16")
+    qw = gpu_pack(dev(w, "bf16"), dq)
+    out = torch.empty((n, k), dtype=torch_dtype(odt), device="cuda")
+    wq.wq_dequantize(qw, out)
+    torch.cuda.synchronize()
+    c, a, c2 = nf4.quantize(host16(w, "bf16"), double_quant=dq)
+    ref = nf4.dequantize(c, a, c2, (n, k), out_dtype=odt)
+    assert np.array_equal(to_np(out), ref)
+
+
+def oracle_y(x, w, xdt, dq=True, rows=None):
+    n, k = w.shape
+    c, a, c2 = nf4.quantize(host16(w, xdt), double_quant=dq)
+    wh = nf4.dequantize(c, a, c2, (n, k), out_dtype=xdt)
+    xs = host16(x, xdt)
+    return linear.reference(xs if rows is None else xs[rows], wh)
+
+
+def run(x, w, xdt, ydt, dq=True, qw=None):
+    m = x.shape[0]
+    n = w.shape[0]
+    if qw is None:
+        qw = gpu_pack(dev(w, xdt), dq)
+    y = torch.empty((m, n), dtype=torch_dtype(ydt), device="cuda")
+    need = wq.wq_linear_w4a16_workspace(m, qw)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda") if need else None
+    wq.wq_linear_w4a16(dev(x, xdt), qw, y, ws)
+    torch.cuda.synchronize()
+    return to_np(y), qw
+
+
+@pytest.mark.parametrize("m,n,k,xdt,ydt,dq", [
+    (1, 300, 1152, "bf16", "f32", True),
+    (1, 1000, 4096, "bf16", "bf16", True),
+    (4, 272, 640, "f16", "f32", False),
+    (16, 512, 2048, "bf16", "f32", True),
+    (40, 300, 1152, "bf16", "f32", True),
+    (512, 1024, 4096, "bf16", "f32", True),
+])
+def test_linear_nf4_parity(m, n, k, xdt, ydt, dq):
+    say(f"linear_nf4 m={m} n={n} k={k} x={xdt} y={ydt} dq={dq}")
+    seed = 300 + m + n
+    x, _ = workloads.activations(m, k, seed, 0, dtype=xdt)
+    w = workloads.weights(n, k, seed, 1, dtype=xdt)
+    y, _ = run(x, w, xdt, ydt, dq)
+    rel = check_close(y, oracle_y(x, w, xdt, dq), ydt)
+    say(f"  max-rel {rel:.2e}")
+
+
+def test_linear_nf4_full_layer():
+    """The 8B-shaped layer (14336 x 4096) at M = 1 (all outputs) and M = 512
+    (32 sampled rows), fp32 output."""
+    say("linear_nf4_full n=14336 k=4096")
+    d = workloads.nf4_layer()
+    qw = None
+    for m in (1, 512):
+        y, qw = run(d["x"][m], d["w"], "bf16", "f32", True, qw)
+        rows = None if m == 1 else np.random.default_rng(1).choice(m, 32, replace=False)
+        ref = oracle_y(d["x"][m], d["w"], "bf16", True, rows)
+        rel = check_close(y if rows is None else y[rows], ref, "f32")
+        say(f"  m={m} max-rel {rel:.2e}")

@@ -1,0 +1,186 @@
+"""GPU parity of the INT4 path against the CPU oracle, through the C ABI.
+
+Codes, scales and zero points must match bit for bit; float outputs must be
+within max|y - y_ref| / max|y_ref| <= 2e-3 of the fp64 oracle computed on the
+oracle's own dequantized weights.  Inputs come from the seeded workload
+generators; the oracle never sees a value produced by the GPU.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_linear_int4_amd as wq
+import workloads
+from oracle import int4, llm_int8, linear
+from gpu_util import check_close, dev, dev_f16, host16, say, to_np, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def edge_weights(n, k, seed, dtype="f16"):
+    """N(0, 0.02) weights with degenerate groups planted in the first rows."""
+    w = host16(workloads.weights(n, k, seed, 1, dtype=dtype), dtype).copy()
+    if n >= 6 and k >= 128:
+        w[0, :128] = 0
+        w[1, :128] = 0.01
+        w[2, :128] = np.abs(w[2, :128]) + 1
+        w[3, :128] = -np.abs(w[3, :128]) - 2
+        w[4, :128] *= 1e-4
+        w[5, :128] *= 1000
+    if dtype == "bf16":
+        return workloads.to_bf16_bits(w)
+    return w.astype(np.float16)
+
+
+def gpu_quantize_int4(w_dev, group=128):
+    n, k = w_dev.shape
+    qw = wq.alloc_int4(n, k, group)
+    wq.wq_quantize_groupwise(w_dev, 4, group, 0, qw.codes, qw.scales, qw.zeros)
+    return qw
+
+
+@pytest.mark.parametrize("n,k,group,dtype", [
+    (64, 512, 128, "f16"),
+    (37, 1152, 128, "f16"),       # ragged rows, odd group count
+    (37, 1152, 128, "bf16"),
+    (16, 640, 64, "f16"),
+    (16, 640, 32, "bf16"),
+    (4096, 4096, 128, "f16"),     # the single-layer decode shape
+    (4096, 11008, 128, "f16"),    # the down-projection shape (86 groups)
+])
+def test_quantize_int4_bitexact(n, k, group, dtype):
+    say(f"quantize_int4 n={n} k={k} group={group} dtype={dtype}")
+    w = edge_weights(n, k, seed=n + k + group, dtype=dtype)
+    qw = gpu_quantize_int4(dev(w, dtype), group)
+    torch.cuda.synchronize()
+    ref_q, ref_s, ref_z = int4.quantize(host16(w, dtype), group)
+    assert np.array_equal(qw.codes.cpu().numpy().view(np.uint32), ref_q)
+    assert np.array_equal(qw.scales.cpu().numpy().view(np.uint16), ref_s.view(np.uint16))
+    assert np.array_equal(qw.zeros.cpu().numpy(), ref_z)
+
+
+@pytest.mark.parametrize("n,k,dtype", [(33, 512, "f16"), (64, 8192, "f16"), (8, 256, "bf16")])
+def test_quantize_int8_rows_bitexact(n, k, dtype):
+    say(f"quantize_int8 n={n} k={k} dtype={dtype}")
+    w = edge_weights(n, k, seed=7 + n, dtype=dtype)
+    wd = dev(w, dtype)
+    qw = wq.alloc_int8(n, k)
+    wq.wq_quantize_groupwise(wd, 8, k, 1, qw.codes, qw.scales)
+    torch.cuda.synchronize()
+    ref_q, ref_s = llm_int8.quantize_rows(host16(w, dtype))
+    assert np.array_equal(qw.codes.cpu().numpy(), ref_q)
+    assert np.array_equal(qw.scales.cpu().numpy(), ref_s)
+
+
+@pytest.mark.parametrize("odt", ["f16", "bf16"])
+def test_dequantize_int4_bitexact(odt):
+    say(f"dequantize_int4 odt={odt}")
+    w = edge_weights(48, 1152, seed=3)
+    qw = gpu_quantize_int4(dev_f16(w))
+    out = torch.empty((48, 1152), dtype=torch_dtype(odt), device="cuda")
+    wq.wq_dequantize(qw, out)
+    torch.cuda.synchronize()
+    ref = int4.dequantize(*int4.quantize(w.astype(np.float32)), 1152, out_dtype=odt)
+    assert np.array_equal(to_np(out), ref)
+
+
+def run_linear(x_np, w_np, xdt, ydt, qw=None):
+    """GPU path: quantize (unless given) + linear, through the ABI."""
+    n, k = w_np.shape
+    m = x_np.shape[0]
+    if qw is None:
+        qw = gpu_quantize_int4(dev(w_np, xdt))
+    x = dev(x_np, xdt)
+    y = torch.empty((m, n), dtype=torch_dtype(ydt), device="cuda")
+    need = wq.wq_linear_w4a16_workspace(m, qw)
+    ws = torch.empty((max(need, 1),), dtype=torch.uint8, device="cuda") if need else None
+    wq.wq_linear_w4a16(x, qw, y, ws)
+    torch.cuda.synchronize()
+    return to_np(y), qw
+
+
+def oracle_linear(x_np, w_np, xdt, rows=None):
+    n, k = w_np.shape
+    wh = int4.dequantize(*int4.quantize(host16(w_np, xdt)), k, out_dtype=xdt)
+    xs = host16(x_np, xdt)
+    if rows is not None:
+        xs = xs[rows]
+    return linear.reference(xs, wh)
+
+
+@pytest.mark.parametrize("m,n,k,xdt,ydt", [
+    (1, 300, 1152, "f16", "f32"),     # ragged n, odd G, single split
+    (1, 4096, 4096, "f16", "f32"),    # full single-layer decode shape (split-K)
+    (1, 4096, 4096, "f16", "f16"),
+    (3, 257, 640, "bf16", "f32"),
+    (5, 520, 2048, "f16", "bf16"),
+    (16, 1000, 2048, "f16", "f32"),
+    (16, 4096, 11008, "f16", "f32"),  # full down-projection shape at M = 16
+    (16, 11008, 4096, "f16", "f16"),  # full gate/up shape at M = 16
+    (16, 777, 1024, "bf16", "f32"),
+])
+def test_linear_skinny_parity(m, n, k, xdt, ydt):
+    say(f"linear_skinny m={m} n={n} k={k} x={xdt} y={ydt}")
+    seed = 100 + m + n
+    x, _ = workloads.activations(m, k, seed, 0, dtype=xdt, outliers=(min(6, k // 128), 20.0, 80.0))
+    w = workloads.weights(n, k, seed, 1, dtype=xdt)
+    y, _ = run_linear(x, w, xdt, ydt)
+    rel = check_close(y, oracle_linear(x, w, xdt), ydt)
+    say(f"  max-rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("m,n,k,xdt,ydt", [
+    (17, 300, 1152, "f16", "f32"),    # smallest GEMM-path m, ragged tiles
+    (130, 129, 256, "f16", "bf16"),
+    (200, 520, 1024, "bf16", "f32"),
+    (256, 1024, 4096, "f16", "f16"),
+])
+def test_linear_gemm_parity(m, n, k, xdt, ydt):
+    say(f"linear_gemm m={m} n={n} k={k} x={xdt} y={ydt}")
+    seed = 200 + m + n
+    x, _ = workloads.activations(m, k, seed, 0, dtype=xdt)
+    w = workloads.weights(n, k, seed, 1, dtype=xdt)
+    y, _ = run_linear(x, w, xdt, ydt)
+    rel = check_close(y, oracle_linear(x, w, xdt), ydt)
+    say(f"  max-rel {rel:.2e}")
+
+
+def test_linear_prefill_full_shape_sampled():
+    """The prefill layer at full size (M = 2048, up-projection 11008 x 4096):
+    every output column of 64 sampled token rows against the oracle."""
+    say("linear_prefill_full m=2048 n=11008 k=4096")
+    layers = workloads.prefill(layers=("up",))
+    name, x, w = layers[0]
+    y, _ = run_linear(x, w, "f16", "f32")
+    rows = np.random.default_rng(0).choice(2048, size=64, replace=False)
+    rel = check_close(y[rows], oracle_linear(x, w, "f16", rows=rows), "f32")
+    say(f"  max-rel {rel:.2e}")
+
+
+def test_linear_with_oracle_packed_weights():
+    """The linear kernels on weights packed by the oracle (isolates them from
+    the quantize kernel)."""
+    say("linear_oracle_packed")
+    m_list = (1, 16, 64)
+    n, k = 272, 1408
+    w = workloads.weights(n, k, 9, 1)
+    q, s, z = int4.quantize(w.astype(np.float32))
+    qw = wq.QuantizedWeight(
+        wq.FMT_INT4_ASYM, n, k, 128,
+        torch.from_numpy(q.view(np.int32)).cuda(),
+        torch.from_numpy(s).cuda(),
+        torch.from_numpy(z).cuda())
+    for m in m_list:
+        x, _ = workloads.activations(m, k, 9, 2)
+        y, _ = run_linear(x, w, "f16", "f32", qw=qw)
+        check_close(y, oracle_linear(x, w, "f16"), "f32")
+
+
+def test_deterministic_repeats():
+    say("determinism")
+    x, _ = workloads.activations(16, 4096, 5, 0)
+    w = workloads.weights(4096, 4096, 5, 1)
+    y1, qw = run_linear(x, w, "f16", "f32")
+    y2, _ = run_linear(x, w, "f16", "f32", qw=qw)
+    assert np.array_equal(y1, y2)

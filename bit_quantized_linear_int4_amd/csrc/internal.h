@@ -58,11 +58,14 @@ hipError_t launch_pack_nf4(const void* w, int wdt, int64_t numel, int double_qua
                            float* absmax_scale, hipStream_t s);
 
 struct W4Plan {
-  int path;      // 0 = decode kernel (m <= 16), 1 = gemm
+  int path;      // 0 = split-K decode kernel, 1 = gemm, 2 = full-K decode kernel
   int tpg;       // row tiles of 16 per workgroup (decode)
-  int gpw;       // groups of 128 per wave (decode); a workgroup covers 4*gpw
+  int gpw;       // split-K kernel: groups of 128 per wave (a workgroup covers 4*gpw)
   int mp;        // activation rows staged in LDS: 1, 4 or 16 (decode)
-  int splits;    // K chunks across workgroups (decode)
+  int splits;    // K chunks across workgroups (split-K decode)
+  int cfg;       // full-K kernel configuration (see plan_w4a16)
+  int phases;    // full-K kernel: activation phases over K
+  int grid;      // full-K kernel: workgroups
   size_t ws;     // workspace bytes (fp32 partial sums when splits > 1)
 };
 W4Plan plan_w4a16(int64_t m, const wq_weight* w);

@@ -295,6 +295,190 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a, Levels lv) {
   }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima, i.e. no wait).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Full-K decode kernel.  Workgroup b owns row tiles b, b + gridDim.x, ...
+// (TPG of them) over the whole K range, so no partial sums leave the
+// workgroup.  The activations (MP rows, m padded) stream into LDS by direct
+// global->LDS loads in phases of CG = NW*GPP groups (NBUF buffers); in each
+// phase every wave multiplies GPP groups of each of its tiles.  All weight
+// loads are issued up front (one round), after the first activation phases,
+// so the weights stream from HBM while the multiply consumes them in order.
+// The NW waves' sums are added in LDS in a fixed order at the end.
+template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int PMAX, int NBUF>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(SkinnyArgs a, Levels lv, int phases) {
+  constexpr int NT = NW * 64;
+  constexpr int CG = NW * GPP;                   // groups per phase
+  constexpr int PCH = CG * 16 * MP;              // 16-byte chunks per phase buffer
+  constexpr int XL = (PCH + NT - 1) / NT;        // direct loads per thread per phase
+  constexpr bool FAST = (FMT == WQ_FMT_INT4_ASYM) && (XDT == WQ_F16);
+  constexpr int RED = NW * TPG * 4 * kWave;      // floats for the final reduction
+  constexpr int SM16 = (NBUF * PCH > RED / 4) ? NBUF * PCH : RED / 4;
+  static_assert(PCH % NT == 0, "every wave issues the same number of direct loads");
+  __shared__ uint4_t xs[SM16];
+  __shared__ float lut[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, kq = lane >> 4;
+  const int ntiles = (a.n + 15) / 16;
+
+  // direct loads of phase p's activation chunk into buffer p % NBUF; layout
+  // [group in phase][16-byte chunk c16][row m]; chunks outside x are loaded
+  // from a clamped address and masked when read
+  auto issue_x = [&](int p) {
+    uint4_t* buf = xs + (p % NBUF) * PCH;
+#pragma unroll
+    for (int r = 0; r < XL; ++r) {
+      const int base = r * NT + wave * 64;       // wave-uniform
+      if (base < PCH) {
+        const int c = base + lane;
+        const int gi = c / (16 * MP), c16 = (c / MP) % 16, m = c % MP;
+        const int g = min(p * CG + gi, a.G - 1), mm = min(m, a.m - 1);
+        const uint16_t* src = a.x + (int64_t)mm * a.k + g * 128 + c16 * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + base), 16, 0, 0);
+      }
+    }
+  };
+  issue_x(0);
+  if (NBUF > 1 && phases > 1) issue_x(1);
+
+  // all weight loads of this wave: PMAX*TPG*GPP units, three loads each,
+  // unconditional (clamped addresses) so the count is known at compile time
+  const uint4_t* q4 = reinterpret_cast<const uint4_t*>(a.codes);
+  const int k32 = a.k / 32;
+  const bool dq = a.scales2 != nullptr;
+  const float* s2p = dq ? a.scales2 : static_cast<const float*>(a.scales);
+  uint4_t wv[PMAX][TPG][GPP];
+  float sv[PMAX][TPG][GPP];
+  uint32_t zv[PMAX][TPG][GPP];
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+#pragma unroll
+    for (int t = 0; t < TPG; ++t) {
+      const int tile = min((int)blockIdx.x + t * (int)gridDim.x, ntiles - 1);
+      const int row = min(tile * 16 + nl, a.n - 1);
+#pragma unroll
+      for (int u = 0; u < GPP; ++u) {
+        const int g = min(p * CG + wave * GPP + u, a.G - 1);
+        wv[p][t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
+        if constexpr (FMT == WQ_FMT_INT4_ASYM) {
+          sv[p][t][u] = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)row * a.G + g]);
+          zv[p][t][u] = a.zeros[(int64_t)row * a.zb + (g >> 1)];
+        } else {
+          // exactly two loads on either path: the first-level absmax (int8
+          // code or fp32) and the second-level scale (unused without double
+          // quantization)
+          const int64_t blk = (int64_t)row * (a.k / 64) + 2 * g + (kq >> 1);
+          const float l2 = s2p[dq ? (blk >> 8) : 0];
+          const float l1 = dq ? (float)static_cast<const int8_t*>(a.scales)[blk]
+                              : static_cast<const float*>(a.scales)[blk];
+          sv[p][t][u] = dq ? l1 * l2 : l1;
+          zv[p][t][u] = 0;
+        }
+      }
+    }
+  }
+  if (FMT == WQ_FMT_NF4 && tid < 16) lut[tid] = lv.v[tid];
+
+  constexpr uint32_t kOne = 0x3C003C00u;
+  const uint4_t ones = {kOne, kOne, kOne, kOne};
+  const int mrow = min(nl, MP - 1);
+  float4_t acc[TPG];
+#pragma unroll
+  for (int t = 0; t < TPG; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+    if (p < phases) {
+      // this wave's direct loads for phase p have landed: everything issued
+      // after them may still be in flight (the next phase's activation
+      // loads and, for the first phases, the weight loads)
+      constexpr int WLOADS = PMAX * TPG * GPP * 3;
+      if (p == 0) {
+        if (NBUF > 1 && phases > 1) vm_wait<XL + WLOADS>(); else vm_wait<WLOADS>();
+      } else if (p == 1 && NBUF > 1) {
+        vm_wait<WLOADS>();
+      } else {
+        if (NBUF > 1 && p + 1 < phases) vm_wait<XL>(); else vm_wait<0>();
+      }
+      __syncthreads();  // ... and so have every other wave's
+      const uint4_t* buf = xs + (p % NBUF) * PCH;
+#pragma unroll
+      for (int u = 0; u < GPP; ++u) {
+        const int gi = wave * GPP + u;
+        const int g = p * CG + gi;
+        const bool live = nl < a.m && g < a.G;
+        uint4_t A[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4_t v = buf[(gi * 16 + kq * 4 + j) * MP + mrow];
+          A[j] = live ? (FAST ? perm_x(v) : v) : uint4_t{0u, 0u, 0u, 0u};
+        }
+        if constexpr (FAST) {
+          float4_t X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) X = mfma16<XDT>(A[j], ones, X);
+#pragma unroll
+          for (int t = 0; t < TPG; ++t) {
+            float4_t tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tmp = mfma16<XDT>(A[j], unpack_biased_f16(wv[p][t][u][j]), tmp);
+            const uint32_t z = (g & 1) ? (zv[p][t][u] >> 4) : (zv[p][t][u] & 15u);
+            const float zb = 1024.0f + (float)z;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(fmaf(-zb, X[e], tmp[e]), sv[p][t][u], acc[t][e]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < TPG; ++t) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              uint4_t b;
+              if constexpr (FMT == WQ_FMT_INT4_ASYM) {
+                const float z = (float)((g & 1) ? (zv[p][t][u] >> 4) : (zv[p][t][u] & 15u));
+                b = dequant_int4_word<XDT>(wv[p][t][u][j], z, sv[p][t][u]);
+              } else {
+                b = dequant_nf4_word<XDT>(wv[p][t][u][j], lut, sv[p][t][u]);
+              }
+              acc[t] = mfma16<XDT>(A[j], b, acc[t]);
+            }
+          }
+        }
+      }
+      if (p + NBUF < phases) {
+        __syncthreads();  // everyone is done with this buffer
+        issue_x(p + NBUF);
+      }
+    }
+  }
+  // fixed-order sum of the NW waves' partial results
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(xs);
+#pragma unroll
+  for (int t = 0; t < TPG; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[((wave * TPG + t) * 4 + e) * kWave + lane] = acc[t][e];
+  __syncthreads();
+  constexpr int NV = TPG * 4 * kWave;
+  for (int i = tid; i < NV; i += NT) {
+    const int te = i / kWave, l = i % kWave, t = te / 4, e = te % 4;
+    const int mm = (l >> 4) * 4 + e;
+    const int tile = (int)blockIdx.x + t * (int)gridDim.x;
+    const int nn = tile * 16 + (l & 15);
+    if (mm < a.m && tile < ntiles && nn < a.n) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[i + w * NV];
+      store_y<YDT>(a.y, (int64_t)mm * a.n + nn, v);
+    }
+  }
+}
+
 template <int YDT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int splits, int64_t mn, void* y) {
@@ -475,6 +659,37 @@ bool launch_skinny(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, dim3 
   return false;
 }
 
+// Full-K decode configurations: NW, TPG, GPP, MP, PMAX, NBUF.
+//  cfg 0..2   m == 1,  K <= 4096:  4 waves, 8 groups/wave, 1 phase, TPG 1/2
+//  cfg 3..4   m <= 4,  K <= 4096
+//  cfg 5..7   m <= 16, K <= 4096:  8 waves, 4 groups/wave, x fully in LDS
+//  cfg 8      m <= 16, K <= 12288: 8 waves, 2 groups/wave, 6 double-buffered phases
+//  cfg 9..10  m <= 4,  K <= 12288: 4 waves, 8 groups/wave, 3 phases
+template <int XDT, int YDT, int FMT>
+bool launch_decode(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.grid);
+#define WQ_DEC(C, NW, TPG, GPP, MP, PMAX, NBUF)                                            \
+  case C:                                                                                  \
+    decode_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, PMAX, NBUF><<<grid, NW * 64, 0, s>>>(  \
+        a, lv, p.phases);                                                                  \
+    return true;
+  switch (p.cfg) {
+    WQ_DEC(0, 4, 1, 8, 1, 1, 1)
+    WQ_DEC(1, 4, 2, 8, 1, 1, 1)
+    WQ_DEC(2, 4, 4, 4, 1, 2, 1)
+    WQ_DEC(3, 4, 1, 8, 4, 1, 1)
+    WQ_DEC(4, 4, 2, 8, 4, 1, 1)
+    WQ_DEC(5, 8, 1, 4, 16, 1, 1)
+    WQ_DEC(6, 8, 2, 4, 16, 1, 1)
+    WQ_DEC(7, 8, 3, 4, 16, 1, 1)
+    WQ_DEC(8, 8, 1, 2, 16, 6, 2)
+    WQ_DEC(9, 4, 1, 8, 1, 3, 1)
+    WQ_DEC(10, 4, 1, 8, 4, 3, 1)
+    default: return false;
+  }
+#undef WQ_DEC
+}
+
 template <int XDT, int YDT>
 hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const float* levels,
                         void* y, void* ws, const W4Plan& p, hipStream_t s) {
@@ -513,6 +728,11 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
   a.zb = (a.G + 1) / 2;
   a.partial = static_cast<float*>(ws);
   a.y = y;
+  if (p.path == 2) {
+    const bool ok = w->fmt == WQ_FMT_NF4 ? launch_decode<XDT, YDT, WQ_FMT_NF4>(a, lv, p, s)
+                                         : launch_decode<XDT, YDT, WQ_FMT_INT4_ASYM>(a, lv, p, s);
+    return ok ? hipGetLastError() : hipErrorInvalidConfiguration;
+  }
   const int ntiles = (int)((w->n + 15) / 16);
   const dim3 grid((unsigned)((ntiles + p.tpg - 1) / p.tpg), (unsigned)p.splits);
   const bool ok = w->fmt == WQ_FMT_NF4 ? launch_skinny<XDT, YDT, WQ_FMT_NF4>(a, lv, p, grid, s)
@@ -540,36 +760,76 @@ hipError_t launch_x(const void* x, int64_t m, const wq_weight* w, const float* l
 
 W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   W4Plan p;
-  p.path = m > 16 ? 1 : 0;
+  p.path = m > 16 ? 1 : 2;
   p.tpg = 1;
   p.gpw = 8;
   p.mp = 1;
   p.splits = 1;
+  p.cfg = 0;
+  p.phases = 1;
+  p.grid = 0;
   p.ws = 0;
   if (p.path == 1) return p;
   const int64_t G = w->k / 128;
   const int64_t ntiles = (w->n + 15) / 16;
   p.mp = m <= 1 ? 1 : (m <= 4 ? 4 : 16);
-  if (p.mp <= 4) {
-    // the activation chunk is small: one workgroup covers up to 32 groups of
-    // its tile, so K <= 4096 needs no split
-    p.gpw = G >= 32 ? 8 : (G > 16 ? 8 : 4);
-    p.splits = (int)((G + 4 * p.gpw - 1) / (4 * p.gpw));
-    p.tpg = ntiles * p.splits >= 2048 ? 2 : 1;
-  } else {
-    // 16 staged rows: 16 groups (64 KB of activations) per workgroup, two
-    // workgroups per CU, and enough tiles per workgroup that the grid is
-    // resident in one scheduling round (<= 512 workgroups)
+  // full-K kernel: one workgroup per CU-share of row tiles, no partial sums
+  struct Cfg { int id, tpg, cg, mp, pmax; };
+  static const Cfg cfgs[] = {
+      {0, 1, 32, 1, 1}, {1, 2, 32, 1, 1}, {2, 4, 16, 1, 2}, {3, 1, 32, 4, 1}, {4, 2, 32, 4, 1},
+      {5, 1, 32, 16, 1}, {6, 2, 32, 16, 1}, {7, 3, 32, 16, 1}, {8, 1, 16, 16, 6},
+      {9, 1, 32, 1, 3}, {10, 1, 32, 4, 3}};
+  int best = -1;
+  int64_t best_grid = 0;
+  for (const Cfg& c : cfgs) {
+    if (c.mp != p.mp) continue;
+    const int64_t phases = (G + c.cg - 1) / c.cg;
+    if (phases > c.pmax) continue;
+    const int64_t grid = (ntiles + c.tpg - 1) / c.tpg;
+    // prefer the fewest phases slots that fit, then about one workgroup per
+    // CU for the 16-row configurations (128 KB of LDS each)
+    const bool fits_round = c.mp == 16 ? grid <= 256 : grid <= 1024;
+    if (best < 0 || (fits_round && !(best_grid <= (p.mp == 16 ? 256 : 1024))) ||
+        (fits_round == (best_grid <= (p.mp == 16 ? 256 : 1024)) && c.pmax < cfgs[best].pmax)) {
+      best = (int)(&c - cfgs);
+      best_grid = grid;
+    }
+  }
+  auto split_k = [&]() {
+    p.path = 0;
     p.gpw = 4;
     p.splits = (int)((G + 15) / 16);
-    int64_t tpg = (ntiles * p.splits + 511) / 512;
+    const int64_t tpg = (ntiles * p.splits + 511) / 512;
     p.tpg = (int)std::max<int64_t>(1, std::min<int64_t>(4, tpg));
+    if (p.mp <= 4) p.tpg = 1;
+  };
+  if (best >= 0) {
+    const Cfg& c = cfgs[best];
+    p.cfg = c.id;
+    p.tpg = c.tpg;
+    p.phases = (int)((G + c.cg - 1) / c.cg);
+    p.grid = (int)((ntiles + c.tpg - 1) / c.tpg);
+  } else {
+    split_k();  // K beyond the full-K configurations
   }
 #ifdef WQ_TUNE_ENV
-  if (const char* e = getenv("WQ_SKINNY")) sscanf(e, "%d,%d,%d", &p.tpg, &p.gpw, &p.mp);
-  p.splits = (int)((G + 4 * p.gpw - 1) / (4 * p.gpw));
+  if (const char* e = getenv("WQ_DECODE")) {
+    int cfg = -2;
+    if (sscanf(e, "%d", &cfg) == 1 && cfg == -1) split_k();
+    if (cfg >= 0) {
+      for (const Cfg& c : cfgs)
+        if (c.id == cfg) {
+          p.path = 2;
+          p.cfg = c.id;
+          p.tpg = c.tpg;
+          p.phases = (int)((G + c.cg - 1) / c.cg);
+          p.grid = (int)((ntiles + c.tpg - 1) / c.tpg);
+        }
+    }
+  }
 #endif
-  if (p.splits > 1) p.ws = (size_t)p.splits * (size_t)m * (size_t)w->n * sizeof(float);
+  if (p.path == 0 && p.splits > 1)
+    p.ws = (size_t)p.splits * (size_t)m * (size_t)w->n * sizeof(float);
   return p;
 }
 

@@ -135,7 +135,7 @@ def test_linear_w4a16_argument_errors():
     assert call(w=_weight(fmt=wq.FMT_INT8_SYM_ROW, group=256)) == UNSUP
     assert call(w=_weight(fmt=wq.FMT_NF4, group=64, zeros=None, scales2=A16, group2=128)) == UNSUP
     # a split-K schedule needs scratch: a missing workspace is reported
-    big = _weight(n=4096, k=11008)
+    big = _weight(n=4096, k=16384)   # beyond the full-K schedules
     need = _lib().wq_linear_w4a16_workspace(16, ctypes.byref(big))
     assert need > 0
     assert call(w=big, m=16) == WS

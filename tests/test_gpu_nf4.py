@@ -91,6 +91,8 @@ def run(x, w, xdt, ydt, dq=True, qw=None):
     (1, 1000, 4096, "bf16", "bf16", True),
     (4, 272, 640, "f16", "f32", False),
     (16, 512, 2048, "bf16", "f32", True),
+    (1, 208, 11008, "bf16", "f32", True),
+    (9, 160, 5120, "bf16", "f32", False),
     (40, 300, 1152, "bf16", "f32", True),
     (512, 1024, 4096, "bf16", "f32", True),
 ])

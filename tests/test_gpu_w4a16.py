@@ -119,6 +119,10 @@ def oracle_linear(x_np, w_np, xdt, rows=None):
     (16, 4096, 11008, "f16", "f32"),  # full down-projection shape at M = 16
     (16, 11008, 4096, "f16", "f16"),  # full gate/up shape at M = 16
     (16, 777, 1024, "bf16", "f32"),
+    (1, 520, 11008, "f16", "f32"),    # three activation phases at m = 1
+    (2, 300, 11008, "f16", "f16"),    # four staged rows, three phases
+    (7, 200, 13824, "f16", "f32"),    # beyond the full-K schedules: split-K path
+    (16, 96, 5120, "bf16", "f32"),    # double-buffered phases, exact bf16 dequant
 ])
 def test_linear_skinny_parity(m, n, k, xdt, ydt):
     say(f"linear_skinny m={m} n={n} k={k} x={xdt} y={ydt}")

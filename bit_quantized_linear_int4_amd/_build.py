@@ -30,7 +30,7 @@ def hipcc():
 
 # -packed-fp32-ops: no v_pk_*_f32 in generated code.
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-x", "hip",
     "-I", INCLUDE, "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

@@ -58,15 +58,16 @@ hipError_t launch_pack_nf4(const void* w, int wdt, int64_t numel, int double_qua
                            float* absmax_scale, hipStream_t s);
 
 struct W4Plan {
-  int path;      // 0 = split-K decode kernel, 1 = gemm, 2 = full-K decode kernel
-  int tpg;       // row tiles of 16 per workgroup (decode)
-  int gpw;       // split-K kernel: groups of 128 per wave (a workgroup covers 4*gpw)
-  int mp;        // activation rows staged in LDS: 1, 4 or 16 (decode)
-  int splits;    // K chunks across workgroups (split-K decode)
-  int cfg;       // full-K kernel configuration (see plan_w4a16)
-  int phases;    // full-K kernel: activation phases over K
-  int grid;      // full-K kernel: workgroups
-  size_t ws;     // workspace bytes (fp32 partial sums when splits > 1)
+  int path;      // 1 = gemm (m > 16), 3 = streaming decode (m <= 16)
+  int tpg;       // decode: row tiles of 16 per workgroup
+  int gpw;       // decode: groups of 128 per wave and phase
+  int mp;        // decode: activation rows staged in LDS: 1, 4 or 16
+  int splits;    // always 1 (no schedule splits K across workgroups)
+  int cfg;       // decode configuration id (see plan_w4a16)
+  int phases;    // decode: phases over K
+  int grid;      // decode: workgroups
+  size_t ws;     // workspace bytes: 0 for every schedule
+  bool szl;      // decode: scales and zero points staged in LDS
 };
 W4Plan plan_w4a16(int64_t m, const wq_weight* w);
 hipError_t launch_w4a16(const void* x, int xdt, int64_t m, const wq_weight* w,

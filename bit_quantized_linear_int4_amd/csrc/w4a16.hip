@@ -6,41 +6,41 @@
 //
 // Two kernel families:
 //
-//  * skinny (m <= 16, decode).  HBM-bound: the packed weights are streamed
-//    once with 16-byte loads.  Each wave owns 16*RT weight rows and a range
-//    of 128-wide groups; every lane loads one 16-byte chunk (32 codes of one
-//    row) per row tile and group.  The multiply runs on the matrix cores
-//    (v_mfma_f32_16x16x32_{f16,bf16}) with the activations (m padded to 16)
-//    as the A operand and the codes as the B operand, so no cross-lane
-//    reduction is needed inside a wave.
+//  * stream (m <= 16, decode).  HBM-bound: the packed codes are streamed
+//    once with 16-byte loads, 16 rows x 64 bytes per wave instruction.  The
+//    multiply runs on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}) with
+//    the activations (m padded to 1, 4 or 16 staged rows) as the A operand
+//    and the codes as the B operand, so no cross-lane reduction is needed
+//    inside a wave.  Each wave walks K in phases and keeps several phases of
+//    loads in flight (a software pipeline per wave, no barriers), so the
+//    multiply of a phase overlaps the loads of the next ones.  The waves'
+//    partial sums are added in LDS in a fixed order: results are
+//    deterministic and no partial sums leave the workgroup.
 //
 //    INT4 codes become 16-bit values with the exponent-bias trick: OR-ing a
-//    nibble into the mantissa of 1024.0 (fp16) or 128.0 (bf16) gives exactly
-//    1024 + q (or 128 + q).  The MFMA accumulates sum_k x_k (B + q_k) over a
-//    group, and the zero point and bias are removed afterwards with the
-//    group's activation sum X = sum_k x_k (itself an MFMA against a ones
-//    operand):  sum_k x_k (q_k - z) s = s * (acc - (B + z) X).
-//    The nibble extraction yields (q0,q4),(q1,q5),(q2,q6),(q3,q7) pairs;
-//    the activations are permuted the same way (the dot product does not
-//    care about the order of k inside one MFMA).
+//    nibble into the mantissa of 1024.0 (fp16) gives exactly 1024 + q.  The
+//    MFMA accumulates sum_k x_k (1024 + q_k) over a group, and the zero
+//    point and bias are removed afterwards with the group's activation sum
+//    X = sum_k x_k (itself an MFMA against a ones operand):
+//    sum_k x_k (q_k - z) s = s * (acc - (1024 + z) X).  The nibble
+//    extraction yields (q0,q4),(q1,q5),(q2,q6),(q3,q7) pairs; the
+//    activations are permuted the same way (the dot product does not care
+//    about the order of k inside one MFMA).  With bf16 activations the codes
+//    are dequantized exactly, (q - z) * s rounded once to bf16.
 //
 //    NF4 codes are looked up in the 16-level table (LDS), multiplied by the
 //    block's absmax and rounded to the activation type, exactly as the
 //    dequantization defines them.
 //
-//    The four waves of a workgroup split the workgroup's group range and
-//    their results are summed in LDS in a fixed order.  When the schedule
-//    also splits K across workgroups, each workgroup writes fp32 partial
-//    sums to the workspace and a second kernel adds them in a fixed order,
-//    so results are deterministic.
-//
 //  * gemm (m > 16, prefill).  MFMA-bound: 128x128 output tiles, the weight
 //    tile is dequantized once into LDS in the activation type and both
 //    operands are read from LDS by four waves (64x64 each).
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -148,153 +148,6 @@ __device__ __forceinline__ uint4_t dequant_nf4_word(uint32_t w, const float* lut
   return b;
 }
 
-// Decode-shaped kernel.  A workgroup owns TPG row tiles (16 rows each) and a
-// chunk of KCG = 4*GPW groups of 128 along K; its four waves take GPW groups
-// each, for all TPG tiles.  Every wave issues all of its weight loads up
-// front (one load round), after the loads that stage the activation chunk
-// (MP rows, zero-padded) into LDS; the multiply consumes the weights in
-// arrival order.  The waves' partial sums are added in LDS in a fixed order.
-// FAST (INT4 weights, fp16 activations) uses the exponent-bias unpack with
-// the per-group correction; the other decoders build exactly rounded
-// dequantized weights.
-template <int XDT, int YDT, int FMT, int TPG, int GPW, int MP>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a, Levels lv) {
-  constexpr int KCG = 4 * GPW;
-  constexpr bool FAST = (FMT == WQ_FMT_INT4_ASYM) && (XDT == WQ_F16);
-  constexpr int XTOT = KCG * 16 * MP;            // staged 16-byte chunks
-  constexpr int XU = (XTOT + 255) / 256;
-  constexpr int RED = 4 * TPG * 4 * kWave;       // floats for the wave reduction
-  constexpr int SMEM16 = XTOT > RED / 4 ? XTOT : RED / 4;
-  __shared__ uint4_t xs[SMEM16];                  // activations, then the reduction
-  __shared__ float lut[16];
-  float* red = reinterpret_cast<float*>(xs);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nl = lane & 15, kq = lane >> 4;
-  const int g0 = blockIdx.y * KCG;
-  const int ntiles = (a.n + 15) / 16;
-  const int tile0 = blockIdx.x * TPG;
-
-  // 1. activation chunk loads (first, so that waiting for them does not wait
-  //    for the weight loads issued after them)
-  uint4_t xv[XU];
-#pragma unroll
-  for (int r = 0; r < XU; ++r) {
-    const int i = tid + 256 * r;
-    const int g = i / (16 * MP), q = i % (16 * MP), m = q / 16, c16 = q % 16;
-    const int gg = min(g0 + g, a.G - 1), mm = min(m, a.m - 1);
-    const uint4_t v = *reinterpret_cast<const uint4_t*>(a.x + (int64_t)mm * a.k + gg * 128 + c16 * 8);
-    xv[r] = (i < XTOT && m < a.m && g0 + g < a.G) ? v : uint4_t{0u, 0u, 0u, 0u};
-  }
-  // 2. all weight loads of this wave
-  const uint4_t* q4 = reinterpret_cast<const uint4_t*>(a.codes);
-  const int k32 = a.k / 32;
-  uint4_t wv[TPG][GPW];
-  float sv[TPG][GPW];
-  uint32_t zv[TPG][GPW];
-#pragma unroll
-  for (int t = 0; t < TPG; ++t) {
-    const int row = min(min(tile0 + t, ntiles - 1) * 16 + nl, a.n - 1);
-#pragma unroll
-    for (int u = 0; u < GPW; ++u) {
-      const int g = min(g0 + wave * GPW + u, a.G - 1);
-      wv[t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
-      if constexpr (FMT == WQ_FMT_INT4_ASYM) {
-        sv[t][u] = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)row * a.G + g]);
-        zv[t][u] = a.zeros[(int64_t)row * a.zb + (g >> 1)];
-      } else {
-        const int64_t blk = (int64_t)row * (a.k / 64) + 2 * g + (kq >> 1);
-        if (a.scales2 != nullptr)
-          sv[t][u] = (float)static_cast<const int8_t*>(a.scales)[blk] * a.scales2[blk >> 8];
-        else
-          sv[t][u] = static_cast<const float*>(a.scales)[blk];
-        zv[t][u] = 0;
-      }
-    }
-  }
-  // 3. stage the activations; layout [group][16-byte chunk c16][row m]
-#pragma unroll
-  for (int r = 0; r < XU; ++r) {
-    const int i = tid + 256 * r;
-    if (i < XTOT) {
-      const int g = i / (16 * MP), q = i % (16 * MP), m = q / 16, c16 = q % 16;
-      xs[(g * 16 + c16) * MP + m] = FAST ? perm_x(xv[r]) : xv[r];
-    }
-  }
-  if (FMT == WQ_FMT_NF4 && tid < 16) lut[tid] = lv.v[tid];
-  __syncthreads();
-
-  // 4. multiply
-  constexpr uint32_t kOne = 0x3C003C00u;
-  const uint4_t ones = {kOne, kOne, kOne, kOne};
-  float4_t acc[TPG];
-#pragma unroll
-  for (int t = 0; t < TPG; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-  const int mrow = min(nl, MP - 1);
-#pragma unroll
-  for (int u = 0; u < GPW; ++u) {
-    const int gl = wave * GPW + u;
-    const int gabs = g0 + gl;
-    uint4_t A[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      A[j] = nl < a.m ? xs[(gl * 16 + kq * 4 + j) * MP + mrow] : uint4_t{0u, 0u, 0u, 0u};
-    if constexpr (FAST) {
-      float4_t X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) X = mfma16<XDT>(A[j], ones, X);
-#pragma unroll
-      for (int t = 0; t < TPG; ++t) {
-        float4_t tmp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tmp = mfma16<XDT>(A[j], unpack_biased_f16(wv[t][u][j]), tmp);
-        const uint32_t z = (gabs & 1) ? (zv[t][u] >> 4) : (zv[t][u] & 15u);
-        const float zb = 1024.0f + (float)z;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(fmaf(-zb, X[e], tmp[e]), sv[t][u], acc[t][e]);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < TPG; ++t) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint4_t b;
-          if constexpr (FMT == WQ_FMT_INT4_ASYM) {
-            const float z = (float)((gabs & 1) ? (zv[t][u] >> 4) : (zv[t][u] & 15u));
-            b = dequant_int4_word<XDT>(wv[t][u][j], z, sv[t][u]);
-          } else {
-            b = dequant_nf4_word<XDT>(wv[t][u][j], lut, sv[t][u]);
-          }
-          acc[t] = mfma16<XDT>(A[j], b, acc[t]);
-        }
-      }
-    }
-  }
-  // 5. add the four waves' sums in a fixed order, then store
-  __syncthreads();  // every wave is done reading the activations
-#pragma unroll
-  for (int t = 0; t < TPG; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) red[((wave * TPG + t) * 4 + e) * kWave + lane] = acc[t][e];
-  __syncthreads();
-  constexpr int NV = TPG * 4 * kWave;
-  const bool splitting = gridDim.y > 1;
-  for (int i = tid; i < NV; i += 256) {
-    const int te = i / kWave, l = i % kWave, t = te / 4, e = te % 4;
-    const int mm = (l >> 4) * 4 + e;
-    const int nn = (tile0 + t) * 16 + (l & 15);
-    if (mm < a.m && nn < a.n) {
-      float v = red[i];
-      v += red[i + NV];
-      v += red[i + 2 * NV];
-      v += red[i + 3 * NV];
-      if (splitting)
-        a.partial[((int64_t)blockIdx.y * a.m + mm) * a.n + nn] = v;
-      else
-        store_y<YDT>(a.y, (int64_t)mm * a.n + nn, v);
-    }
-  }
-}
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima, i.e. no wait).
@@ -304,61 +157,127 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Full-K decode kernel.  Workgroup b owns row tiles b, b + gridDim.x, ...
-// (TPG of them) over the whole K range, so no partial sums leave the
-// workgroup.  The activations (MP rows, m padded) stream into LDS by direct
-// global->LDS loads in phases of CG = NW*GPP groups (NBUF buffers); in each
-// phase every wave multiplies GPP groups of each of its tiles.  All weight
-// loads are issued up front (one round), after the first activation phases,
-// so the weights stream from HBM while the multiply consumes them in order.
-// The NW waves' sums are added in LDS in a fixed order at the end.
-template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int PMAX, int NBUF>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(SkinnyArgs a, Levels lv, int phases) {
-  constexpr int NT = NW * 64;
-  constexpr int CG = NW * GPP;                   // groups per phase
-  constexpr int PCH = CG * 16 * MP;              // 16-byte chunks per phase buffer
-  constexpr int XL = (PCH + NT - 1) / NT;        // direct loads per thread per phase
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would make every wave wait for all of its outstanding global loads (the
+// direct-to-LDS loads are counted with them), which serializes the weight
+// stream behind the first phase.  Callers wait for exactly the loads that
+// must have landed (vm_wait) before calling it; the empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform count known only at run time, by
+// binary search over the immediates (counts above the hardware maximum wait
+// for that maximum, which waits for more loads than asked: safe).
+template <int LO, int HI>
+__device__ __forceinline__ void vm_wait_range(int n) {
+  if constexpr (LO == HI) {
+    vm_wait<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) vm_wait_range<LO, MID>(n); else vm_wait_range<MID + 1, HI>(n);
+  }
+}
+__device__ __forceinline__ void vm_wait_n(int n) { vm_wait_range<0, 63>(n); }
+
+// Streaming decode kernel.  Workgroup b owns row tiles b, b + gridDim.x, ...
+// (TPG of them) over the whole K range.  K is walked in phases of
+// CG = NW*GPP groups; in phase p wave w owns groups p*CG + w*GPP + [0, GPP)
+// for all TPG tiles, so no data is shared between the waves until the final
+// sum.  Each wave stages the activations of its own groups (MP rows, padded)
+// into a private LDS ring of NBUF phase buffers with direct global->LDS
+// loads, and keeps the codes of NBUF phases in registers.  Loads are issued
+// phase by phase (activations, then codes), NBUF phases ahead of the
+// multiply, so the multiply of a phase starts as soon as that phase's own
+// loads have landed and the loads of later phases keep streaming meanwhile.
+//
+// SZL (INT4): the workgroup's scales and zero points -- 16 consecutive rows
+// of each, contiguous in HBM -- are staged into LDS up front with a few
+// 1 KB direct loads instead of two small loads per code load.  It needs
+// 16-byte aligned scale and zero buffers whose sizes are multiples of 16.
+//
+// The 16-byte chunk c16 of activation row m sits in slot c16 ^ (m & 15) of
+// the row, so the 16 rows an MFMA operand read touches fall in different LDS
+// banks.  LDS is sized at launch (stream_lds_bytes).
+template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL>
+__global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv, int phases) {
+  constexpr int CG = NW * GPP;                             // groups per phase
+  constexpr int XS = (MP * GPP * 16 + 63) / 64 * 64;       // slots per wave buffer
+  constexpr int XI = XS / 64;                              // direct loads per phase
+  constexpr int LPU = SZL ? 1 : 3;                         // loads per code unit
+  constexpr int WU = TPG * GPP * LPU;                      // code-side loads per phase
   constexpr bool FAST = (FMT == WQ_FMT_INT4_ASYM) && (XDT == WQ_F16);
-  constexpr int RED = NW * TPG * 4 * kWave;      // floats for the final reduction
-  constexpr int SM16 = (NBUF * PCH > RED / 4) ? NBUF * PCH : RED / 4;
-  static_assert(PCH % NT == 0, "every wave issues the same number of direct loads");
-  __shared__ uint4_t xs[SM16];
+  static_assert(!SZL || FMT == WQ_FMT_INT4_ASYM, "staged scales are INT4 only");
+  extern __shared__ uint4_t dsm[];
   __shared__ float lut[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, kq = lane >> 4;
   const int ntiles = (a.n + 15) / 16;
+  uint4_t* const ring = dsm + wave * NBUF * XS;
+  // staged scales / zeros: per tile SCB and ZCB bytes (multiples of 1 KB)
+  const int SCB = (32 * a.G + 1023) / 1024 * 1024;
+  const int ZCB = (16 * a.zb + 1023) / 1024 * 1024;
+  uint8_t* const scl = reinterpret_cast<uint8_t*>(dsm + NW * NBUF * XS);
+  uint8_t* const zcl = scl + TPG * SCB;
 
-  // direct loads of phase p's activation chunk into buffer p % NBUF; layout
-  // [group in phase][16-byte chunk c16][row m]; chunks outside x are loaded
-  // from a clamped address and masked when read
+  if constexpr (FMT == WQ_FMT_NF4) {
+    if (tid < 16) lut[tid] = lv.v[tid];
+    __syncthreads();   // before any load is in flight: costs no wait
+  }
+  if constexpr (SZL) {
+    // 1 KB direct loads of the tiles' scale and zero rows, spread over the
+    // waves; chunks past the end of a buffer reload its last 16 bytes
+    const int nsc = SCB / 1024, nzc = ZCB / 1024, per = nsc + nzc;
+    const int64_t sbytes = (int64_t)a.n * a.G * 2, zbytes = (int64_t)a.n * a.zb;
+    const uint8_t* sbase = static_cast<const uint8_t*>(a.scales);
+    for (int i = wave; i < TPG * per; i += NW) {
+      const int t = i / per, j = i % per;
+      const int tile = min((int)blockIdx.x + t * (int)gridDim.x, ntiles - 1);
+      const bool isz = j >= nsc;
+      const int jj = isz ? j - nsc : j;
+      const int64_t off = (int64_t)tile * 16 * (isz ? a.zb : 2 * a.G) + jj * 1024 + lane * 16;
+      const int64_t lim = (isz ? zbytes : sbytes) - 16;
+      const uint8_t* src = (isz ? a.zeros : sbase) + min(off, lim);
+      uint8_t* dst = (isz ? zcl + t * ZCB : scl + t * SCB) + jj * 1024;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  // activation loads of phase p into ring buffer p % NBUF: lane l of load i
+  // fills slot 64*i + l, i.e. row m = slot / (16*GPP), group gl, chunk c16
+  // (swizzled); slots past the wave's rows, groups past K and rows past m
+  // read clamped addresses and are never used
   auto issue_x = [&](int p) {
-    uint4_t* buf = xs + (p % NBUF) * PCH;
+    uint4_t* buf = ring + (p % NBUF) * XS;
 #pragma unroll
-    for (int r = 0; r < XL; ++r) {
-      const int base = r * NT + wave * 64;       // wave-uniform
-      if (base < PCH) {
-        const int c = base + lane;
-        const int gi = c / (16 * MP), c16 = (c / MP) % 16, m = c % MP;
-        const int g = min(p * CG + gi, a.G - 1), mm = min(m, a.m - 1);
-        const uint16_t* src = a.x + (int64_t)mm * a.k + g * 128 + c16 * 8;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + base), 16, 0, 0);
-      }
+    for (int i = 0; i < XI; ++i) {
+      const int sl = i * 64 + lane;
+      const int m = min(sl / (16 * GPP), MP - 1);
+      const int gl = (sl / 16) % GPP;
+      const int c16 = (sl % 16) ^ (m & 15);
+      const int g = min(p * CG + wave * GPP + gl, a.G - 1);
+      const int mm = min(m, a.m - 1);
+      __builtin_amdgcn_global_load_lds(a.x + (int64_t)mm * a.k + g * 128 + c16 * 8,
+                                       (lds_void_t*)(buf + i * 64), 16, 0, 0);
     }
   };
-  issue_x(0);
-  if (NBUF > 1 && phases > 1) issue_x(1);
 
-  // all weight loads of this wave: PMAX*TPG*GPP units, three loads each,
-  // unconditional (clamped addresses) so the count is known at compile time
   const uint4_t* q4 = reinterpret_cast<const uint4_t*>(a.codes);
   const int k32 = a.k / 32;
   const bool dq = a.scales2 != nullptr;
   const float* s2p = dq ? a.scales2 : static_cast<const float*>(a.scales);
-  uint4_t wv[PMAX][TPG][GPP];
-  float sv[PMAX][TPG][GPP];
-  uint32_t zv[PMAX][TPG][GPP];
-#pragma unroll
-  for (int p = 0; p < PMAX; ++p) {
+  uint4_t wv[NBUF][TPG][GPP];
+  float sv[NBUF][TPG][GPP];
+  uint32_t zv[NBUF][TPG][GPP];
+  // code loads of phase p into register slot b (plus, without staged
+  // scales, the unit's scale and zero point or NF4 absmax levels)
+  auto issue_w = [&](int p, auto bc) {
+    constexpr int b = decltype(bc)::value;
 #pragma unroll
     for (int t = 0; t < TPG; ++t) {
       const int tile = min((int)blockIdx.x + t * (int)gridDim.x, ntiles - 1);
@@ -366,58 +285,66 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(SkinnyArgs a, Levels lv
 #pragma unroll
       for (int u = 0; u < GPP; ++u) {
         const int g = min(p * CG + wave * GPP + u, a.G - 1);
-        wv[p][t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
-        if constexpr (FMT == WQ_FMT_INT4_ASYM) {
-          sv[p][t][u] = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)row * a.G + g]);
-          zv[p][t][u] = a.zeros[(int64_t)row * a.zb + (g >> 1)];
+        wv[b][t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
+        if constexpr (SZL) {
+        } else if constexpr (FMT == WQ_FMT_INT4_ASYM) {
+          sv[b][t][u] = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)row * a.G + g]);
+          zv[b][t][u] = a.zeros[(int64_t)row * a.zb + (g >> 1)];
         } else {
-          // exactly two loads on either path: the first-level absmax (int8
-          // code or fp32) and the second-level scale (unused without double
-          // quantization)
+          // the first-level absmax (int8 code or fp32) and the second-level
+          // scale (a harmless reload of element 0 without double quantization)
           const int64_t blk = (int64_t)row * (a.k / 64) + 2 * g + (kq >> 1);
           const float l2 = s2p[dq ? (blk >> 8) : 0];
           const float l1 = dq ? (float)static_cast<const int8_t*>(a.scales)[blk]
                               : static_cast<const float*>(a.scales)[blk];
-          sv[p][t][u] = dq ? l1 * l2 : l1;
-          zv[p][t][u] = 0;
+          sv[b][t][u] = dq ? l1 * l2 : l1;
+          zv[b][t][u] = 0;
         }
       }
     }
-  }
-  if (FMT == WQ_FMT_NF4 && tid < 16) lut[tid] = lv.v[tid];
+  };
+
+  // prologue: phases 0 .. NBUF-1 (always issued; phases past the end load
+  // clamped addresses, which keeps the load count fixed)
+  [&]<int... B>(std::integer_sequence<int, B...>) {
+    ((issue_x(B), issue_w(B, std::integral_constant<int, B>{})), ...);
+  }(std::make_integer_sequence<int, NBUF>{});
+  asm volatile("" ::: "memory");
 
   constexpr uint32_t kOne = 0x3C003C00u;
   const uint4_t ones = {kOne, kOne, kOne, kOne};
-  const int mrow = min(nl, MP - 1);
+  const int mrow = min(nl, MP - 1);     // rows past m duplicate a staged row; not stored
   float4_t acc[TPG];
 #pragma unroll
   for (int t = 0; t < TPG; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const int issued_max = max(phases, NBUF) - 1;   // last phase whose loads get issued
+
+  auto step = [&](int p, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    // loads issued after this phase's activation loads: its code loads and
+    // every later phase issued so far
+    const int later = min(p + NBUF - 1, issued_max) - p;
+    vm_wait_n(WU + later * (XI + WU));
+    if (SZL && p == 0) wg_barrier();   // every wave's staged scale/zero loads have landed
+    asm volatile("" ::: "memory");
+    const uint4_t* buf = ring + b * XS + mrow * (16 * GPP);
 #pragma unroll
-  for (int p = 0; p < PMAX; ++p) {
-    if (p < phases) {
-      // this wave's direct loads for phase p have landed: everything issued
-      // after them may still be in flight (the next phase's activation
-      // loads and, for the first phases, the weight loads)
-      constexpr int WLOADS = PMAX * TPG * GPP * 3;
-      if (p == 0) {
-        if (NBUF > 1 && phases > 1) vm_wait<XL + WLOADS>(); else vm_wait<WLOADS>();
-      } else if (p == 1 && NBUF > 1) {
-        vm_wait<WLOADS>();
-      } else {
-        if (NBUF > 1 && p + 1 < phases) vm_wait<XL>(); else vm_wait<0>();
-      }
-      __syncthreads();  // ... and so have every other wave's
-      const uint4_t* buf = xs + (p % NBUF) * PCH;
+    for (int u = 0; u < GPP; ++u) {
+      const int g = p * CG + wave * GPP + u;
+      if (g < a.G) {
+        if constexpr (SZL) {
 #pragma unroll
-      for (int u = 0; u < GPP; ++u) {
-        const int gi = wave * GPP + u;
-        const int g = p * CG + gi;
-        const bool live = nl < a.m && g < a.G;
+          for (int t = 0; t < TPG; ++t) {
+            const uint16_t sc = *reinterpret_cast<const uint16_t*>(scl + t * SCB + (nl * a.G + g) * 2);
+            sv[b][t][u] = f16_bits_to_f32(sc);
+            zv[b][t][u] = zcl[t * ZCB + nl * a.zb + (g >> 1)];
+          }
+        }
         uint4_t A[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4_t v = buf[(gi * 16 + kq * 4 + j) * MP + mrow];
-          A[j] = live ? (FAST ? perm_x(v) : v) : uint4_t{0u, 0u, 0u, 0u};
+          const uint4_t v = buf[u * 16 + ((kq * 4 + j) ^ (mrow & 15))];
+          A[j] = FAST ? perm_x(v) : v;
         }
         if constexpr (FAST) {
           float4_t X = {0.f, 0.f, 0.f, 0.f};
@@ -427,45 +354,56 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(SkinnyArgs a, Levels lv
           for (int t = 0; t < TPG; ++t) {
             float4_t tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tmp = mfma16<XDT>(A[j], unpack_biased_f16(wv[p][t][u][j]), tmp);
-            const uint32_t z = (g & 1) ? (zv[p][t][u] >> 4) : (zv[p][t][u] & 15u);
+            for (int j = 0; j < 4; ++j) tmp = mfma16<XDT>(A[j], unpack_biased_f16(wv[b][t][u][j]), tmp);
+            const uint32_t z = (g & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u);
             const float zb = 1024.0f + (float)z;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(fmaf(-zb, X[e], tmp[e]), sv[p][t][u], acc[t][e]);
+            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(fmaf(-zb, X[e], tmp[e]), sv[b][t][u], acc[t][e]);
           }
         } else {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              uint4_t b;
+              uint4_t bw;
               if constexpr (FMT == WQ_FMT_INT4_ASYM) {
-                const float z = (float)((g & 1) ? (zv[p][t][u] >> 4) : (zv[p][t][u] & 15u));
-                b = dequant_int4_word<XDT>(wv[p][t][u][j], z, sv[p][t][u]);
+                const float z = (float)((g & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u));
+                bw = dequant_int4_word<XDT>(wv[b][t][u][j], z, sv[b][t][u]);
               } else {
-                b = dequant_nf4_word<XDT>(wv[p][t][u][j], lut, sv[p][t][u]);
+                bw = dequant_nf4_word<XDT>(wv[b][t][u][j], lut, sv[b][t][u]);
               }
-              acc[t] = mfma16<XDT>(A[j], b, acc[t]);
+              acc[t] = mfma16<XDT>(A[j], bw, acc[t]);
             }
           }
         }
       }
-      if (p + NBUF < phases) {
-        __syncthreads();  // everyone is done with this buffer
-        issue_x(p + NBUF);
-      }
     }
+    // refill this ring slot with phase p + NBUF (this wave's reads of it are
+    // complete: their values fed the MFMAs above)
+    if (p + NBUF < phases) {
+      asm volatile("" ::: "memory");
+      issue_x(p + NBUF);
+      issue_w(p + NBUF, bc);
+      asm volatile("" ::: "memory");
+    }
+  };
+  for (int p0 = 0; p0 < phases; p0 += NBUF) {
+    [&]<int... B>(std::integer_sequence<int, B...>) {
+      ((p0 + B < phases ? step(p0 + B, std::integral_constant<int, B>{}) : void()), ...);
+    }(std::make_integer_sequence<int, NBUF>{});
   }
+  vm_wait<0>();   // clamped loads of unused prologue phases
+
   // fixed-order sum of the NW waves' partial results
   __syncthreads();
-  float* red = reinterpret_cast<float*>(xs);
+  float* red = reinterpret_cast<float*>(dsm);
 #pragma unroll
   for (int t = 0; t < TPG; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[((wave * TPG + t) * 4 + e) * kWave + lane] = acc[t][e];
   __syncthreads();
   constexpr int NV = TPG * 4 * kWave;
-  for (int i = tid; i < NV; i += NT) {
+  for (int i = tid; i < NV; i += NW * 64) {
     const int te = i / kWave, l = i % kWave, t = te / 4, e = te % 4;
     const int mm = (l >> 4) * 4 + e;
     const int tile = (int)blockIdx.x + t * (int)gridDim.x;
@@ -479,14 +417,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(SkinnyArgs a, Levels lv
   }
 }
 
-template <int YDT>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
-                                                            int splits, int64_t mn, void* y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= mn) return;
-  float v = part[i];
-  for (int s = 1; s < splits; ++s) v += part[(int64_t)s * mn + i];
-  store_y<YDT>(y, i, v);
+// Dynamic LDS bytes of one stream_kernel workgroup.
+inline size_t stream_lds_bytes(int nw, int tpg, int gpp, int mp, int nbuf, bool szl, int G, int zb) {
+  const size_t xs = (size_t)((mp * gpp * 16 + 63) / 64 * 64) * 16;
+  size_t b = (size_t)nw * nbuf * xs;
+  if (szl) b += (size_t)tpg * ((32 * G + 1023) / 1024 * 1024 + (16 * zb + 1023) / 1024 * 1024);
+  const size_t red = (size_t)nw * tpg * 4 * 64 * 4;
+  return b > red ? b : red;
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -637,57 +574,54 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
 }
 
 // ---------------------------------------------------------------- launch
-template <int XDT, int YDT, int FMT, int TPG, int GPW, int MP>
-void launch_skinny_t(const SkinnyArgs& a, const Levels& lv, dim3 grid, hipStream_t s) {
-  skinny_kernel<XDT, YDT, FMT, TPG, GPW, MP><<<grid, 256, 0, s>>>(a, lv);
-}
-
-// Schedules compiled for the decode kernel: (TPG, GPW, MP).
-template <int XDT, int YDT, int FMT>
-bool launch_skinny(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, dim3 grid,
-                   hipStream_t s) {
-#define WQ_CASE(T, W, M)                                                       \
-  if (p.tpg == T && p.gpw == W && p.mp == M) {                                 \
-    launch_skinny_t<XDT, YDT, FMT, T, W, M>(a, lv, grid, s);                   \
-    return true;                                                               \
+// Streaming decode configurations: NW, TPG, GPP, MP, NBUF.
+template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL>
+hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
+  auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL>;
+  const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, a.G, a.zb);
+  if (lds > 160 * 1024 - 256) return hipErrorInvalidConfiguration;
+  // raise the dynamic LDS limit of this instantiation when a launch needs
+  // more than the default (the static NF4 table shares the 160 KB)
+  static std::atomic<size_t> allowed{64 * 1024};
+  if (lds > allowed.load(std::memory_order_relaxed)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    size_t cur = allowed.load(std::memory_order_relaxed);
+    while (lds > cur && !allowed.compare_exchange_weak(cur, lds)) {
+    }
   }
-  WQ_CASE(1, 8, 1) WQ_CASE(2, 8, 1) WQ_CASE(1, 8, 4) WQ_CASE(2, 8, 4)
-  WQ_CASE(1, 4, 1) WQ_CASE(1, 4, 4)
-  WQ_CASE(1, 4, 16) WQ_CASE(2, 4, 16) WQ_CASE(3, 4, 16) WQ_CASE(4, 4, 16)
-  WQ_CASE(1, 2, 16) WQ_CASE(2, 2, 16)
-#undef WQ_CASE
-  return false;
+  kern<<<dim3((unsigned)p.grid), NW * 64, lds, s>>>(a, lv, p.phases);
+  return hipGetLastError();
 }
 
-// Full-K decode configurations: NW, TPG, GPP, MP, PMAX, NBUF.
-//  cfg 0..2   m == 1,  K <= 4096:  4 waves, 8 groups/wave, 1 phase, TPG 1/2
-//  cfg 3..4   m <= 4,  K <= 4096
-//  cfg 5..7   m <= 16, K <= 4096:  8 waves, 4 groups/wave, x fully in LDS
-//  cfg 8      m <= 16, K <= 12288: 8 waves, 2 groups/wave, 6 double-buffered phases
-//  cfg 9..10  m <= 4,  K <= 12288: 4 waves, 8 groups/wave, 3 phases
 template <int XDT, int YDT, int FMT>
-bool launch_decode(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
-  const dim3 grid((unsigned)p.grid);
-#define WQ_DEC(C, NW, TPG, GPP, MP, PMAX, NBUF)                                            \
+hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
+#define WQ_STR(C, NW, TPG, GPP, MP, NBUF)                                                  \
   case C:                                                                                  \
-    decode_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, PMAX, NBUF><<<grid, NW * 64, 0, s>>>(  \
-        a, lv, p.phases);                                                                  \
-    return true;
+    if constexpr (FMT == WQ_FMT_INT4_ASYM) {                                               \
+      if (p.szl) return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, true>(a, lv, p, s); \
+    }                                                                                      \
+    return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false>(a, lv, p, s);
   switch (p.cfg) {
-    WQ_DEC(0, 4, 1, 8, 1, 1, 1)
-    WQ_DEC(1, 4, 2, 8, 1, 1, 1)
-    WQ_DEC(2, 4, 4, 4, 1, 2, 1)
-    WQ_DEC(3, 4, 1, 8, 4, 1, 1)
-    WQ_DEC(4, 4, 2, 8, 4, 1, 1)
-    WQ_DEC(5, 8, 1, 4, 16, 1, 1)
-    WQ_DEC(6, 8, 2, 4, 16, 1, 1)
-    WQ_DEC(7, 8, 3, 4, 16, 1, 1)
-    WQ_DEC(8, 8, 1, 2, 16, 6, 2)
-    WQ_DEC(9, 4, 1, 8, 1, 3, 1)
-    WQ_DEC(10, 4, 1, 8, 4, 3, 1)
-    default: return false;
+    WQ_STR(20, 4, 1, 4, 1, 2)
+    WQ_STR(21, 4, 1, 2, 1, 4)
+    WQ_STR(22, 8, 1, 1, 1, 4)
+    WQ_STR(23, 4, 2, 2, 1, 4)
+    WQ_STR(24, 4, 1, 1, 4, 4)
+    WQ_STR(25, 8, 1, 1, 4, 4)
+    WQ_STR(26, 4, 2, 1, 4, 4)
+    WQ_STR(27, 8, 3, 1, 16, 4)
+    WQ_STR(28, 4, 3, 1, 16, 4)
+    WQ_STR(29, 8, 1, 1, 16, 4)
+    WQ_STR(30, 4, 2, 1, 16, 4)
+    WQ_STR(31, 8, 2, 1, 16, 4)
+    WQ_STR(32, 4, 1, 1, 16, 4)
+    WQ_STR(33, 4, 1, 4, 1, 4)
+    WQ_STR(34, 8, 1, 2, 1, 4)
+    default: return hipErrorInvalidConfiguration;
   }
-#undef WQ_DEC
+#undef WQ_STR
 }
 
 template <int XDT, int YDT>
@@ -726,24 +660,10 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
   a.k = (int)w->k;
   a.G = (int)(w->k / 128);
   a.zb = (a.G + 1) / 2;
-  a.partial = static_cast<float*>(ws);
   a.y = y;
-  if (p.path == 2) {
-    const bool ok = w->fmt == WQ_FMT_NF4 ? launch_decode<XDT, YDT, WQ_FMT_NF4>(a, lv, p, s)
-                                         : launch_decode<XDT, YDT, WQ_FMT_INT4_ASYM>(a, lv, p, s);
-    return ok ? hipGetLastError() : hipErrorInvalidConfiguration;
-  }
-  const int ntiles = (int)((w->n + 15) / 16);
-  const dim3 grid((unsigned)((ntiles + p.tpg - 1) / p.tpg), (unsigned)p.splits);
-  const bool ok = w->fmt == WQ_FMT_NF4 ? launch_skinny<XDT, YDT, WQ_FMT_NF4>(a, lv, p, grid, s)
-                                       : launch_skinny<XDT, YDT, WQ_FMT_INT4_ASYM>(a, lv, p, grid, s);
-  if (!ok) return hipErrorInvalidConfiguration;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t mn = m * w->n;
-  splitk_reduce_kernel<YDT><<<dim3((unsigned)((mn + 255) / 256)), 256, 0, s>>>(
-      static_cast<const float*>(ws), p.splits, mn, y);
-  return hipGetLastError();
+  (void)ws;
+  return w->fmt == WQ_FMT_NF4 ? launch_stream<XDT, YDT, WQ_FMT_NF4>(a, lv, p, s)
+                              : launch_stream<XDT, YDT, WQ_FMT_INT4_ASYM>(a, lv, p, s);
 }
 
 template <int XDT>
@@ -759,77 +679,67 @@ hipError_t launch_x(const void* x, int64_t m, const wq_weight* w, const float* l
 }  // namespace
 
 W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
+  // Streaming decode configurations (NW waves, TPG row tiles, GPP groups per
+  // wave and phase, MP staged activation rows); NBUF is 4 except for cfg 20.
+  struct SCfg { int id, nw, tpg, gpp, mp; };
+  static const SCfg scfgs[] = {
+      {20, 4, 1, 4, 1}, {21, 4, 1, 2, 1}, {22, 8, 1, 1, 1}, {23, 4, 2, 2, 1}, {24, 4, 1, 1, 4},
+      {25, 8, 1, 1, 4}, {26, 4, 2, 1, 4}, {27, 8, 3, 1, 16}, {28, 4, 3, 1, 16}, {29, 8, 1, 1, 16},
+      {30, 4, 2, 1, 16}, {31, 8, 2, 1, 16}, {32, 4, 1, 1, 16}, {33, 4, 1, 4, 1}, {34, 8, 1, 2, 1}};
   W4Plan p;
-  p.path = m > 16 ? 1 : 2;
+  p.path = m > 16 ? 1 : 3;
   p.tpg = 1;
-  p.gpw = 8;
+  p.gpw = 1;
   p.mp = 1;
   p.splits = 1;
   p.cfg = 0;
   p.phases = 1;
   p.grid = 0;
   p.ws = 0;
+  p.szl = w->fmt == WQ_FMT_INT4_ASYM && ((uintptr_t)w->scales % 16) == 0 &&
+          ((uintptr_t)w->zeros % 16) == 0 && (w->n * (w->k / 128) * 2) % 16 == 0 &&
+          (w->n * ((w->k / 128 + 1) / 2)) % 16 == 0;
   if (p.path == 1) return p;
   const int64_t G = w->k / 128;
   const int64_t ntiles = (w->n + 15) / 16;
-  p.mp = m <= 1 ? 1 : (m <= 4 ? 4 : 16);
-  // full-K kernel: one workgroup per CU-share of row tiles, no partial sums
-  struct Cfg { int id, tpg, cg, mp, pmax; };
-  static const Cfg cfgs[] = {
-      {0, 1, 32, 1, 1}, {1, 2, 32, 1, 1}, {2, 4, 16, 1, 2}, {3, 1, 32, 4, 1}, {4, 2, 32, 4, 1},
-      {5, 1, 32, 16, 1}, {6, 2, 32, 16, 1}, {7, 3, 32, 16, 1}, {8, 1, 16, 16, 6},
-      {9, 1, 32, 1, 3}, {10, 1, 32, 4, 3}};
-  int best = -1;
-  int64_t best_grid = 0;
-  for (const Cfg& c : cfgs) {
-    if (c.mp != p.mp) continue;
-    const int64_t phases = (G + c.cg - 1) / c.cg;
-    if (phases > c.pmax) continue;
-    const int64_t grid = (ntiles + c.tpg - 1) / c.tpg;
-    // prefer the fewest phases slots that fit, then about one workgroup per
-    // CU for the 16-row configurations (128 KB of LDS each)
-    const bool fits_round = c.mp == 16 ? grid <= 256 : grid <= 1024;
-    if (best < 0 || (fits_round && !(best_grid <= (p.mp == 16 ? 256 : 1024))) ||
-        (fits_round == (best_grid <= (p.mp == 16 ? 256 : 1024)) && c.pmax < cfgs[best].pmax)) {
-      best = (int)(&c - cfgs);
-      best_grid = grid;
-    }
-  }
-  auto split_k = [&]() {
-    p.path = 0;
-    p.gpw = 4;
-    p.splits = (int)((G + 15) / 16);
-    const int64_t tpg = (ntiles * p.splits + 511) / 512;
-    p.tpg = (int)std::max<int64_t>(1, std::min<int64_t>(4, tpg));
-    if (p.mp <= 4) p.tpg = 1;
-  };
-  if (best >= 0) {
-    const Cfg& c = cfgs[best];
-    p.cfg = c.id;
-    p.tpg = c.tpg;
-    p.phases = (int)((G + c.cg - 1) / c.cg);
-    p.grid = (int)((ntiles + c.tpg - 1) / c.tpg);
+  // measured on MI355X (graph-replayed calls of the 7B/8B decode shapes):
+  //  m = 1: one group per wave and phase, two when K is long;
+  //  m <= 4: eight waves, one tile;
+  //  m <= 16: one workgroup per CU (128 KB of activation ring), as many
+  //           tiles per workgroup as that takes (at most 3).
+  int cfg;
+  if (m <= 1) {
+    cfg = G >= 64 ? 34 : 22;
+  } else if (m <= 4) {
+    cfg = 25;
   } else {
-    split_k();  // K beyond the full-K configurations
+    const int64_t tpg = (ntiles + 255) / 256;
+    cfg = tpg >= 3 ? 27 : (tpg == 2 ? 31 : 29);
   }
 #ifdef WQ_TUNE_ENV
   if (const char* e = getenv("WQ_DECODE")) {
-    int cfg = -2;
-    if (sscanf(e, "%d", &cfg) == 1 && cfg == -1) split_k();
-    if (cfg >= 0) {
-      for (const Cfg& c : cfgs)
-        if (c.id == cfg) {
-          p.path = 2;
-          p.cfg = c.id;
-          p.tpg = c.tpg;
-          p.phases = (int)((G + c.cg - 1) / c.cg);
-          p.grid = (int)((ntiles + c.tpg - 1) / c.tpg);
-        }
-    }
+    int c = -1;
+    if (sscanf(e, "%d", &c) == 1)
+      for (const SCfg& sc : scfgs)
+        if (sc.id == c) cfg = c;
   }
 #endif
-  if (p.path == 0 && p.splits > 1)
-    p.ws = (size_t)p.splits * (size_t)m * (size_t)w->n * sizeof(float);
+  for (const SCfg& sc : scfgs)
+    if (sc.id == cfg) {
+      p.cfg = sc.id;
+      p.tpg = sc.tpg;
+      p.gpw = sc.gpp;
+      p.mp = sc.mp;
+      p.phases = (int)((G + sc.nw * sc.gpp - 1) / (sc.nw * sc.gpp));
+      p.grid = (int)((ntiles + sc.tpg - 1) / sc.tpg);
+      // staged scales must fit beside the activation ring
+      if (p.szl) {
+        const size_t lds = (size_t)sc.nw * 4 * ((sc.mp * sc.gpp * 16 + 63) / 64 * 64) * 16 +
+                           (size_t)sc.tpg * ((32 * G + 1023) / 1024 * 1024 +
+                                             (16 * ((G + 1) / 2) + 1023) / 1024 * 1024);
+        if (lds > 160 * 1024 - 256) p.szl = false;
+      }
+    }
   return p;
 }
 

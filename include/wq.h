@@ -32,7 +32,8 @@
  *    unspecified (but memory-safe) results.
  *  - Rounding: every "round" is round-half-to-even; every division is an
  *    IEEE fp32 division; 16-bit conversions round to nearest even.
- *  - The library keeps no mutable global state; it is thread-safe.
+ *  - The library's only mutable global state is the per-kernel LDS limit it
+ *    raises once (atomically) on first use; calls are thread-safe.
  */
 #ifndef WQ_H
 #define WQ_H

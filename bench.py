@@ -1,26 +1,32 @@
-"""Benchmark of the W4A16 quantized linear path on one MI355X.
+"""Benchmark of the quantized linear path on one MI355X.
 
 Default workload: the 7B-style MLP decode batch -- M = 16 tokens through
 gate [11008 x 4096], up [11008 x 4096] and down [4096 x 11008] INT4 layers
-(group 128, fp16 scale, 4-bit zero point), fp16 activations.  One step is the
-three dequant-GEMV calls.  Weights are quantized on the GPU once (offline
-step, outside the timed region) and replicated into enough distinct copies
-(>= 512 MB) that every step reads weights the 256 MB Infinity Cache has not
-just served; inputs are resident in HBM when timing starts.
+(group 128, fp16 scale, 4-bit zero point), fp16 activations, fp16 outputs.
+One step is the three dequant-GEMV calls.  Weights are quantized on the GPU
+once (offline step, outside the timed region) and replicated into enough
+distinct copies (>= 512 MB) that successive steps read weights the 256 MB
+Infinity Cache has not just served; inputs are resident in HBM when timing
+starts.
+
+Timing.  The K timed steps are captured into one HIP graph and replayed
+once between two HIP events on the capture stream (warmup: W eager steps,
+then one untimed replay that also uploads the graph).  The dominant kernel
+is timed the same way in a region of its own: K launches of it alone, back
+to back, so its average launch duration is comparable with the
+rocprofv3 kernel trace of the same command.
 
 Reported value: effective HBM GB/s = algorithmic bytes of one step (packed
-codes + fp16 scales + 4-bit zeros + x + y, each read or written once) / step
-time.  The "roofline" object covers the dominant kernel (the decode GEMV),
-timed per call with HIP events recorded on the stream the library launches
-on; "cpu_baseline" times the CPU oracle on a bounded sample of the same
-layers.
+codes + scales + zero points + x + y, each read or written once) / step time
+(TFLOP/s = 2*M*N*K / step time for the GEMM workloads).
 
 Other workloads (--workload): decode_m1 (M = 1, 4096 x 4096), prefill
-(M = 2048 through q, k, v, o and up; TFLOP/s), nf4_m1 / nf4_m512 (NF4 14336 x
-4096, bf16), int8_70b (LLM.int8 at 28672 x 8192, M = 256).
+(M = 2048 through q, k, v, o and up), nf4_m1 / nf4_m512 (NF4 14336 x 4096,
+bf16), int8_70b (LLM.int8 at 28672 x 8192, M = 256).
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,123 +39,243 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 MFMA16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 512 << 20
+METRIC = "W4A16 g128 linear: effective HBM GB/s (M=1) and TFLOP/s (M=2048), % roofline"
+KERNEL_SOURCES = {
+    "stream": "bit_quantized_linear_int4_amd/csrc/w4a16.hip",
+    "gemm": "bit_quantized_linear_int4_amd/csrc/w4a16.hip",
+    "int8": "bit_quantized_linear_int4_amd/csrc/int8.hip",
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# ----------------------------------------------------------------- workloads
+def _copies_needed(per_copy_bytes):
+    return max(1, -(-ROTATE_BYTES // max(1, per_copy_bytes)))
+
+
 class Workload:
-    """One step = a list of library calls; bytes/flops are algorithmic."""
+    """One step = a list of calls.  Work (bytes or flops) is algorithmic:
+    what the method has to move or compute, not what the kernels do."""
 
-    name = ""
     unit = "GB/s"
-    metric = "W4A16 g128 linear: effective HBM GB/s (M=1) and TFLOP/s (M=2048), % roofline"
     dtype = "f16"
-
-    def setup(self):
-        raise NotImplementedError
-
-    def calls(self, step):
-        raise NotImplementedError
-
-
-def _int4_layer(wq, torch, w_np):
-    n, k = w_np.shape
-    qw = wq.alloc_int4(n, k)
-    wq.wq_quantize_groupwise(torch.from_numpy(w_np).cuda(), 4, 128, 0, qw.codes, qw.scales, qw.zeros)
-    return qw
-
-
-def _ws(wq, torch, m, qw):
-    need = wq.wq_linear_w4a16_workspace(m, qw)
-    return torch.empty((need,), dtype=torch.uint8, device="cuda") if need else None
-
-
-def _copies(qw_list, per_copy_bytes):
-    reps = max(1, -(-ROTATE_BYTES // max(1, per_copy_bytes)))
-    out = [qw_list]
-    for _ in range(reps - 1):
-        out.append([q.clone() for q in qw_list])
-    return out
-
-
-class W4Layers(Workload):
-    """A sequence of INT4 layers applied to their own inputs (decode or prefill)."""
+    kernel = "stream"        # family of the dominant kernel
+    kernel_desc = ""
 
     def __init__(self, name, layers, unit):
         self.name = name
-        self.layers_np = layers          # list of (layer name, x, w)
+        self.layers_np = layers
         self.unit = unit
+
+    # to be provided: setup(), step_calls(copy), dominant_calls(copy),
+    # work_per_step(), dominant_work(), cpu_sample(), config()
+
+
+def _int4_weight(wq, torch, w_np):
+    n, k = w_np.shape
+    qw = wq.alloc_int4(n, k)
+    wq.wq_quantize_groupwise(torch.from_numpy(w_np).cuda(), 4, 128, 0, qw.codes, qw.scales,
+                             qw.zeros)
+    return qw
+
+
+class W4Layers(Workload):
+    """INT4 layers, each applied to its own seeded input (decode or prefill)."""
 
     def setup(self):
         import torch
         import bit_quantized_linear_int4_amd as wq
         self.wq = wq
-        base = []
-        self.xs, self.ys, self.wss = [], [], []
-        self.bytes_per_call, self.flops_per_call = [], []
-        for name, x, w in self.layers_np:
-            qw = _int4_layer(wq, torch, w)
+        base, self.xs, self.ys = [], [], []
+        self.bytes, self.flops = [], []
+        for _, x, w in self.layers_np:
+            qw = _int4_weight(wq, torch, w)
             base.append(qw)
             m, n, k = x.shape[0], w.shape[0], w.shape[1]
             self.xs.append(torch.from_numpy(x).cuda())
             self.ys.append(torch.empty((m, n), dtype=torch.float16, device="cuda"))
-            self.wss.append(_ws(wq, torch, m, qw))
-            self.bytes_per_call.append(qw.nbytes() + x.size * 2 + m * n * 2)
-            self.flops_per_call.append(2 * m * n * k)
+            self.bytes.append(qw.nbytes() + x.size * 2 + m * n * 2)
+            self.flops.append(2 * m * n * k)
+            assert wq.wq_linear_w4a16_workspace(m, qw) == 0
         torch.cuda.synchronize()
-        self.copies = _copies(base, sum(q.nbytes() for q in base))
+        reps = _copies_needed(sum(q.nbytes() for q in base))
+        self.copies = [base] + [[q.clone() for q in base] for _ in range(reps - 1)]
         torch.cuda.synchronize()
-        self.m = [x.shape[0] for _, x, _ in self.layers_np]
+        # dominant kernel: the layer shape that takes most of the step
+        # (gate/up share one kernel configuration in the decode step)
+        shapes = [(x.shape[0], w.shape[0], w.shape[1]) for _, x, w in self.layers_np]
+        groups = {}
+        for i, s in enumerate(shapes):
+            groups.setdefault(s, []).append(i)
+        self.dom = max(groups.values(), key=lambda idx: (len(idx), -idx[0]))
+        m, n, k = shapes[self.dom[0]]
+        fam = "stream dequant-GEMV" if m <= 16 else "dequant-GEMM"
+        self.kernel = "stream" if m <= 16 else "gemm"
+        names = "/".join(self.layers_np[i][0] for i in self.dom)
+        self.kernel_desc = f"w4a16 {fam} ({names}: M={m}, N={n}, K={k})"
 
-    def calls(self, step):
-        wq = self.wq
-        ws = self.copies[step % len(self.copies)]
-        return [(lambda i=i: wq.wq_linear_w4a16(self.xs[i], ws[i], self.ys[i], self.wss[i]))
-                for i in range(len(ws))]
+    def _call(self, copy, i):
+        wq, ws = self.wq, self.copies[copy % len(self.copies)]
+        return lambda: wq.wq_linear_w4a16(self.xs[i], ws[i], self.ys[i], None)
+
+    def step_calls(self, copy):
+        return [self._call(copy, i) for i in range(len(self.layers_np))]
+
+    def dominant_calls(self, copy):
+        return [self._call(copy, i) for i in self.dom]
 
     def work_per_step(self):
-        return sum(self.bytes_per_call) if self.unit == "GB/s" else sum(self.flops_per_call)
+        return sum(self.bytes) if self.unit == "GB/s" else sum(self.flops)
 
-    def dominant(self):
-        if self.unit == "GB/s":
-            return ("w4a16 skinny dequant-GEMV (HIP events per call)",
-                    sum(self.bytes_per_call) / len(self.bytes_per_call), "hbm")
-        return ("w4a16 dequant-GEMM (HIP events per call)",
-                sum(self.flops_per_call) / len(self.flops_per_call), "mfma")
+    def dominant_work(self):
+        per = self.bytes if self.unit == "GB/s" else self.flops
+        return per[self.dom[0]]
 
     def cpu_sample(self):
-        """Oracle: dequantize + fp64 product on the first rows of every layer."""
+        """Oracle: quantize, dequantize and fp64 product on the first rows of
+        every layer."""
         import numpy as np
         from oracle import int4, linear
-        layers = []
-        for name, x, w in self.layers_np:
-            rows = max(16, w.shape[0] // 32)
-            layers.append((x, w[:rows]))
-        pre = [(x, int4.quantize(w)) + (w.shape,) for x, w in layers]
+        frac = 32 if self.unit == "GB/s" else 256
+        sample = [(nm, x, w[:max(16, w.shape[0] // frac)]) for nm, x, w in self.layers_np]
 
         def run():
-            for x, (q, s, z), shp in pre:
-                wh = int4.dequantize(q, s, z, shp[1])
+            for _, x, w in sample:
+                q, s, z = int4.quantize(w)
+                wh = int4.dequantize(q, s, z, w.shape[1])
                 linear.reference(x.astype(np.float32), wh)
         work = 0
-        for x, (q, s, z), shp in pre:
-            m, n, k = x.shape[0], shp[0], shp[1]
+        for _, x, w in sample:
+            m, n, k = x.shape[0], w.shape[0], w.shape[1]
             if self.unit == "GB/s":
-                work += q.nbytes + s.nbytes + z.nbytes + x.size * 2 + m * n * 2
+                g = k // 128
+                work += n * k // 2 + n * g * 2 + n * ((g + 1) // 2) + x.size * 2 + m * n * 2
             else:
                 work += 2 * m * n * k
-        desc = ", ".join(f"{nm} first {max(16, w.shape[0] // 32)} rows"
-                         for nm, x, w in self.layers_np)
-        return run, work, desc
+        desc = ", ".join(f"{nm} first {w.shape[0]} rows" for nm, _, w in sample)
+        return run, work, desc + "; oracle quantize + dequantize + fp64 product"
 
     def config(self):
         return {"workload": self.name,
                 "layers": [{"name": nm, "m": int(x.shape[0]), "n": int(w.shape[0]),
                             "k": int(w.shape[1])} for nm, x, w in self.layers_np],
                 "format": "INT4 asymmetric, group 128, fp16 scale, 4-bit zero",
+                "weight_copies": len(self.copies)}
+
+
+class NF4Layer(Workload):
+    dtype = "bf16"
+
+    def setup(self):
+        import torch
+        import bit_quantized_linear_int4_amd as wq
+        self.wq = wq
+        (_, x, w), = self.layers_np
+        n, k = w.shape
+        m = x.shape[0]
+        wd = torch.from_numpy(w.view("uint16").astype("int16")).cuda().view(torch.bfloat16)
+        qw = wq.alloc_nf4(n, k, double_quant=True)
+        wq.wq_pack_nf4(wd, 64, True, 256, qw.codes, qw.scales, qw.scales2)
+        self.x = torch.from_numpy(x.view("uint16").astype("int16")).cuda().view(torch.bfloat16)
+        self.y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        reps = _copies_needed(qw.nbytes())
+        self.copies = [qw] + [qw.clone() for _ in range(reps - 1)]
+        self.nbytes = qw.nbytes() + m * k * 2 + m * n * 2
+        self.nflops = 2 * m * n * k
+        self.kernel = "stream" if m <= 16 else "gemm"
+        fam = "stream dequant-GEMV" if m <= 16 else "dequant-GEMM"
+        self.kernel_desc = f"nf4 {fam} (M={m}, N={n}, K={k})"
+
+    def step_calls(self, copy):
+        qw = self.copies[copy % len(self.copies)]
+        return [lambda: self.wq.wq_linear_w4a16(self.x, qw, self.y, None)]
+
+    dominant_calls = step_calls
+
+    def work_per_step(self):
+        return self.nbytes if self.unit == "GB/s" else self.nflops
+
+    dominant_work = work_per_step
+
+    def cpu_sample(self):
+        import numpy as np
+        from oracle import nf4, linear, numerics
+        (_, x, w), = self.layers_np
+        rows = max(64, w.shape[0] // (64 if self.unit == "GB/s" else 512))
+        ws = numerics.bf16_bits_to_f32(w[:rows])
+        xs = numerics.bf16_bits_to_f32(x)
+
+        def run():
+            c, a, c2 = nf4.quantize(ws, double_quant=True)
+            wh = nf4.dequantize(c, a, c2, ws.shape, out_dtype="bf16")
+            linear.reference(xs, wh)
+        m, k = x.shape
+        work = (rows * k // 2 + rows * k // 64 + m * k * 2 + m * rows * 2
+                if self.unit == "GB/s" else 2 * m * rows * k)
+        return run, work, f"first {rows} rows; oracle NF4 quantize + dequantize + fp64 product"
+
+    def config(self):
+        (_, x, w), = self.layers_np
+        return {"workload": self.name, "m": int(x.shape[0]), "n": int(w.shape[0]),
+                "k": int(w.shape[1]),
+                "format": "NF4 block 64, int8 double-quantized absmax (block 256)",
+                "weight_copies": len(self.copies)}
+
+
+class Int8Layer(Workload):
+    kernel = "int8"
+
+    def setup(self):
+        import torch
+        import bit_quantized_linear_int4_amd as wq
+        self.wq = wq
+        (_, x, w), = self.layers_np
+        n, k = w.shape
+        m = x.shape[0]
+        qw = wq.alloc_int8(n, k)
+        wq.wq_quantize_groupwise(torch.from_numpy(w).cuda(), 8, k, 1, qw.codes, qw.scales)
+        self.x = torch.from_numpy(x).cuda()
+        self.y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        need = wq.wq_linear_int8_decomp_workspace(m, k)
+        self.ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        reps = _copies_needed(qw.nbytes())
+        self.copies = [qw] + [qw.clone() for _ in range(reps - 1)]
+        self.nbytes = qw.nbytes() + m * k * 2 + m * n * 2
+        self.kernel_desc = f"LLM.int8 decomposition (M={m}, N={n}, K={k})"
+
+    def step_calls(self, copy):
+        qw = self.copies[copy % len(self.copies)]
+        return [lambda: self.wq.wq_linear_int8_decomp(self.x, qw, 6.0, self.y, self.ws)]
+
+    dominant_calls = step_calls
+
+    def work_per_step(self):
+        return self.nbytes
+
+    dominant_work = work_per_step
+
+    def cpu_sample(self):
+        from oracle import llm_int8
+        (_, x, w), = self.layers_np
+        rows = 512
+        wsub = w[:rows]
+
+        def run():
+            qw, sw = llm_int8.quantize_rows(wsub)
+            llm_int8.linear(x, qw, sw, 6.0)
+        m, k = x.shape
+        work = rows * k + rows * 4 + m * k * 2 + m * rows * 2
+        return run, work, f"first {rows} rows; oracle LLM.int8 quantize + decomposition"
+
+    def config(self):
+        (_, x, w), = self.layers_np
+        return {"workload": self.name, "m": int(x.shape[0]), "n": int(w.shape[0]),
+                "k": int(w.shape[1]), "threshold": 6.0,
+                "format": "int8 per output row (absmax/127), fp16 outlier columns",
                 "weight_copies": len(self.copies)}
 
 
@@ -162,91 +288,194 @@ def make_workload(name):
         return W4Layers("decode_m1_4096x4096", [("proj", d["x"], d["w"])], "GB/s")
     if name == "prefill":
         return W4Layers("prefill_m2048_7b", workloads.prefill(), "TFLOP/s")
+    if name in ("nf4_m1", "nf4_m512"):
+        d = workloads.nf4_layer()
+        m = 1 if name == "nf4_m1" else 512
+        return NF4Layer(f"nf4_8b_m{m}", [("w", d["x"][m], d["w"])],
+                        "GB/s" if m == 1 else "TFLOP/s")
+    if name == "int8_70b":
+        d = workloads.int8_70b()
+        return Int8Layer("llm_int8_70b_m256", [("w", d["x"], d["w"])], "GB/s")
     raise SystemExit(f"unknown workload {name}")
 
 
 # ------------------------------------------------------------------- timing
-def time_workload(wl, steps, warmup):
+def timed_graph(calls_for_step, count, warm_eager):
+    """Capture `count` steps into one graph; run `warm_eager` eager steps
+    and one untimed replay; return the replay time in ms (HIP events on the
+    capture stream)."""
     import torch
-    for s in range(warmup):
-        for c in wl.calls(s):
+    for s in range(warm_eager):
+        for c in calls_for_step(s):
             c()
     torch.cuda.synchronize()
-    ncalls = len(wl.calls(0))
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps * ncalls)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps * ncalls)]
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for s in range(count):
+            for c in calls_for_step(s):
+                c()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    i = 0
-    for s in range(steps):
-        for c in wl.calls(warmup + s):
-            starts[i].record()
-            c()
-            ends[i].record()
-            i += 1
+    graph.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    per_call = [starts[j].elapsed_time(ends[j]) for j in range(i)]  # ms
-    return (t1 - t0) / steps * 1e3, sum(per_call) / len(per_call)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
 
 
-def cpu_baseline(wl, unit, budget_s=15.0):
+def traffic_from_profile(wl):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, KERNEL_SOURCES[wl.kernel])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha:
+        return None
     try:
-        import threadpoolctl
-        limiter = threadpoolctl.threadpool_limits
-    except Exception:  # pragma: no cover
-        limiter = None
-    cores = os.cpu_count() or 1
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(wl, budget_s):
+    import threadpoolctl
+    cores = cpu_threads()
     run, work, desc = wl.cpu_sample()
-    ctx = limiter(limits=cores) if limiter else None
     reps, t = 0, 0.0
-    if ctx:
-        ctx.__enter__()
-    try:
+    with threadpoolctl.threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         while True:
             run()
             reps += 1
             t = time.perf_counter() - t0
-            if t > budget_s or reps >= 50:
+            if t > budget_s or reps >= 100:
                 break
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    scale = 1e9 if unit == "GB/s" else 1e12
-    return {"value": round(work * reps / t / scale, 4), "unit": unit, "cores": cores,
-            "kind": "oracle",
-            "sample": f"{desc}; dequantize + fp64 product, {reps} repetitions in {t:.1f} s"}
+    scale = 1e9 if wl.unit == "GB/s" else 1e12
+    return {"value": round(work * reps / t / scale, 6), "unit": wl.unit, "cores": cores,
+            "kind": "oracle", "sample": f"{desc}; {reps} repetitions in {t:.1f} s"}
+
+
+def copy_probe(mib):
+    """A plain device copy of known size (reads and writes `mib` MiB per
+    launch), run 5 times: the reference dispatch for scaling the rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    a = torch.ones((mib << 20) // 2, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def summarize_pmc(fetch_csv, write_csv, kernel_substr, copy_mib, out_path, command):
+    """Write the traffic summary of the dominant kernel from two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE), each counter scaled by what it
+    reads for the plain copy of `copy_mib` MiB."""
+    import csv
+    import statistics
+
+    def per_dispatch(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return rows
+
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = per_dispatch(path, counter)
+        copy = [v for k, vs in rows.items() if "copy" in k.lower() or "elementwise" in k.lower()
+                for v in vs]
+        copy = sorted(copy)[-5:]                  # the five probe copies (largest dispatches)
+        factor = statistics.median(copy) / (copy_mib * 1024.0)   # counter units per KiB moved
+        kern = [v for k, vs in rows.items() if kernel_substr in k for v in vs]
+        res[counter] = (statistics.mean(kern) / factor * 1024.0, factor, len(kern))
+    fetch, write = res["FETCH_SIZE"][0], res["WRITE_SIZE"][0]
+    src = os.path.join(ROOT, KERNEL_SOURCES["stream" if "stream" in kernel_substr else
+                                            ("int8" if "int8" in kernel_substr else "gemm")])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    with open(out_path, "w") as f:
+        f.write(f"# HBM traffic of one launch of the kernels matching '{kernel_substr}',\n")
+        f.write("# from two rocprofv3 --pmc runs, each counter scaled by its reading for a\n")
+        f.write(f"# plain device copy of {copy_mib} MiB (reads and writes {copy_mib} MiB).\n")
+        f.write(f"# command: {command}\n")
+        f.write(f"fetch_factor_per_kib={res['FETCH_SIZE'][1]:.6f}\n")
+        f.write(f"write_factor_per_kib={res['WRITE_SIZE'][1]:.6f}\n")
+        f.write(f"dispatches={res['FETCH_SIZE'][2]}\n")
+        f.write(f"fetch_bytes_per_launch={fetch:.0f}\n")
+        f.write(f"write_bytes_per_launch={write:.0f}\n")
+        f.write(f"hbm_bytes_per_launch={fetch + write:.0f}\n")
+        f.write(f"source={os.path.relpath(src, ROOT)}\n")
+        f.write(f"source_sha256={sha}\n")
+    print(open(out_path).read())
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        # --summarize-pmc FETCH_CSV WRITE_CSV KERNEL_SUBSTR COPY_MIB OUT "COMMAND"
+        a = sys.argv[2:]
+        summarize_pmc(a[0], a[1], a[2], int(a[3]), a[4], a[5])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mlp_decode")
+    ap.add_argument("--workload", default="mlp_decode",
+                    choices=["mlp_decode", "decode_m1", "prefill", "nf4_m1", "nf4_m512",
+                             "int8_70b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB five times (the reference "
+                         "dispatch for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this library's path is "
-              "single-GPU. Run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): the quantized linear "
+              "path here is single-GPU; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     wl = make_workload(args.workload)
     log(f"[bench] setting up {wl.name}")
     wl.setup()
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
-    ms_step, ms_call = time_workload(wl, args.steps, args.warmup)
-    work = wl.work_per_step()
+    ms = timed_graph(wl.step_calls, args.steps, args.warmup)
+    ms_step = ms / args.steps
+    log(f"[bench] timing the dominant kernel: {wl.kernel_desc}")
+    ndom = len(wl.dominant_calls(0))
+    ms_dom = timed_graph(wl.dominant_calls, args.steps, 2)
+    launches = args.steps * ndom
+    us_launch = ms_dom * 1e3 / launches
     scale = 1e9 if wl.unit == "GB/s" else 1e12
-    value = work / (ms_step * 1e-3) / scale
-    kname, per_call_work, bound = wl.dominant()
-    achieved = per_call_work / (ms_call * 1e-3) / scale
+    value = wl.work_per_step() / (ms_step * 1e-3) / scale
+    achieved = wl.dominant_work() / (us_launch * 1e-6) / scale
+    bound = "hbm" if wl.unit == "GB/s" else "mfma"
     peak = HBM_PEAK_GBS if bound == "hbm" else MFMA16_PEAK_TFLOPS
     out = {
-        "metric": wl.metric,
+        "metric": METRIC,
         "value": round(value, 3),
         "unit": wl.unit,
         "n_gpus": 1,
@@ -257,16 +486,18 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with fixed outlier channels)",
+        "data": "synthetic: seeded N(0,0.02) weights, N(0,1) activations with fixed outlier "
+                "channels (decode), random-init layers of the 7B/8B/70B shapes",
         "config": wl.config(),
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
-                     "unit": wl.unit, "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": kname, "avg_call_us": round(ms_call * 1e3, 3),
-                     "work_per_call": per_call_work},
+                     "unit": wl.unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic_from_profile(wl),
+                     "kernel": wl.kernel_desc, "avg_launch_us": round(us_launch, 3),
+                     "work_per_launch": wl.dominant_work(), "launches": launches},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
-        out["cpu_baseline"] = cpu_baseline(wl, wl.unit, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

@@ -62,11 +62,12 @@ struct W4Plan {
   int tpg;       // decode: row tiles of 16 per workgroup
   int gpw;       // decode: groups of 128 per wave and phase
   int mp;        // decode: activation rows staged in LDS: 1, 4 or 16
-  int splits;    // always 1 (no schedule splits K across workgroups)
+  int splits;    // decode: K slices across workgroups (partials summed by a second kernel)
+  int kslice;    // decode: groups per K slice
   int cfg;       // decode configuration id (see plan_w4a16)
   int phases;    // decode: phases over K
   int grid;      // decode: workgroups
-  size_t ws;     // workspace bytes: 0 for every schedule
+  size_t ws;     // workspace bytes: splits * m * n fp32 partial sums when splits > 1
   bool szl;      // decode: scales and zero points staged in LDS
 };
 W4Plan plan_w4a16(int64_t m, const wq_weight* w);

@@ -150,6 +150,22 @@ __device__ __forceinline__ uint4_t dequant_nf4_word(uint32_t w, const float* lut
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds + 16*l (lds is wave-uniform, passed in M0).
+// Issued from inline asm on purpose: the compiler's wait-count bookkeeping
+// treats these loads as completing out of order with ordinary loads and then
+// falls back to waiting for every outstanding load.  Hidden from it, its
+// automatic waits for ordinary loads count only ordinary loads, which can
+// only make them stricter (each direct load it does not see is one more
+// outstanding load that must finish first); the kernels wait for their
+// direct loads themselves (vm_wait with counts that include them) before any
+// LDS read of the data.  No output register, so nothing is left in flight
+// behind the compiler's back but LDS bytes the explicit waits cover.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, lds_void_t* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(l) : "memory");
+}
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima, i.e. no wait).
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -190,7 +206,7 @@ __device__ __forceinline__ void vm_wait_n(int n) { vm_wait_range<0, 63>(n); }
 // sum.  Each wave stages the activations of its own groups (MP rows, padded)
 // into a private LDS ring of NBUF phase buffers with direct global->LDS
 // loads, and keeps the codes of NBUF phases in registers.  Loads are issued
-// phase by phase (activations, then codes), NBUF phases ahead of the
+// phase by phase (codes, then activations), NBUF phases ahead of the
 // multiply, so the multiply of a phase starts as soon as that phase's own
 // loads have landed and the loads of later phases keep streaming meanwhile.
 //
@@ -203,7 +219,8 @@ __device__ __forceinline__ void vm_wait_n(int n) { vm_wait_range<0, 63>(n); }
 // the row, so the 16 rows an MFMA operand read touches fall in different LDS
 // banks.  LDS is sized at launch (stream_lds_bytes).
 template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL>
-__global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv, int phases) {
+__global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv, int phases,
+                                                         int kslice) {
   constexpr int CG = NW * GPP;                             // groups per phase
   constexpr int XS = (MP * GPP * 16 + 63) / 64 * 64;       // slots per wave buffer
   constexpr int XI = XS / 64;                              // direct loads per phase
@@ -217,6 +234,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, kq = lane >> 4;
   const int ntiles = (a.n + 15) / 16;
+  // this workgroup's K slice: groups [gbeg, gend)
+  const int gbeg = (int)blockIdx.y * kslice;
+  const int gend = min(a.G, gbeg + kslice);
   uint4_t* const ring = dsm + wave * NBUF * XS;
   // staged scales / zeros: per tile SCB and ZCB bytes (multiples of 1 KB)
   const int SCB = (32 * a.G + 1023) / 1024 * 1024;
@@ -243,7 +263,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       const int64_t lim = (isz ? zbytes : sbytes) - 16;
       const uint8_t* src = (isz ? a.zeros : sbase) + min(off, lim);
       uint8_t* dst = (isz ? zcl + t * ZCB : scl + t * SCB) + jj * 1024;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+      lds_dma16(src, (lds_void_t*)dst);
     }
     asm volatile("" ::: "memory");
   }
@@ -260,10 +280,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       const int m = min(sl / (16 * GPP), MP - 1);
       const int gl = (sl / 16) % GPP;
       const int c16 = (sl % 16) ^ (m & 15);
-      const int g = min(p * CG + wave * GPP + gl, a.G - 1);
+      const int g = min(gbeg + p * CG + wave * GPP + gl, a.G - 1);
       const int mm = min(m, a.m - 1);
-      __builtin_amdgcn_global_load_lds(a.x + (int64_t)mm * a.k + g * 128 + c16 * 8,
-                                       (lds_void_t*)(buf + i * 64), 16, 0, 0);
+      lds_dma16(a.x + (int64_t)mm * a.k + g * 128 + c16 * 8, (lds_void_t*)(buf + i * 64));
     }
   };
 
@@ -284,7 +303,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       const int row = min(tile * 16 + nl, a.n - 1);
 #pragma unroll
       for (int u = 0; u < GPP; ++u) {
-        const int g = min(p * CG + wave * GPP + u, a.G - 1);
+        const int g = min(gbeg + p * CG + wave * GPP + u, a.G - 1);
         wv[b][t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
         if constexpr (SZL) {
         } else if constexpr (FMT == WQ_FMT_INT4_ASYM) {
@@ -307,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // prologue: phases 0 .. NBUF-1 (always issued; phases past the end load
   // clamped addresses, which keeps the load count fixed)
   [&]<int... B>(std::integer_sequence<int, B...>) {
-    ((issue_x(B), issue_w(B, std::integral_constant<int, B>{})), ...);
+    ((issue_w(B, std::integral_constant<int, B>{}), issue_x(B)), ...);
   }(std::make_integer_sequence<int, NBUF>{});
   asm volatile("" ::: "memory");
 
@@ -321,17 +340,18 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
 
   auto step = [&](int p, auto bc) {
     constexpr int b = decltype(bc)::value;
-    // loads issued after this phase's activation loads: its code loads and
-    // every later phase issued so far
+    // loads issued after this phase's activation loads: those of every later
+    // phase issued so far (each phase issues its code loads, then its
+    // activation loads)
     const int later = min(p + NBUF - 1, issued_max) - p;
-    vm_wait_n(WU + later * (XI + WU));
+    vm_wait_n(later * (XI + WU));
     if (SZL && p == 0) wg_barrier();   // every wave's staged scale/zero loads have landed
     asm volatile("" ::: "memory");
     const uint4_t* buf = ring + b * XS + mrow * (16 * GPP);
 #pragma unroll
     for (int u = 0; u < GPP; ++u) {
-      const int g = p * CG + wave * GPP + u;
-      if (g < a.G) {
+      const int g = gbeg + p * CG + wave * GPP + u;
+      if (g < gend) {
         if constexpr (SZL) {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
@@ -382,8 +402,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     // complete: their values fed the MFMAs above)
     if (p + NBUF < phases) {
       asm volatile("" ::: "memory");
-      issue_x(p + NBUF);
       issue_w(p + NBUF, bc);
+      issue_x(p + NBUF);
       asm volatile("" ::: "memory");
     }
   };
@@ -412,9 +432,23 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += red[i + w * NV];
-      store_y<YDT>(a.y, (int64_t)mm * a.n + nn, v);
+      if (gridDim.y > 1)
+        a.partial[((int64_t)blockIdx.y * a.m + mm) * a.n + nn] = v;
+      else
+        store_y<YDT>(a.y, (int64_t)mm * a.n + nn, v);
     }
   }
+}
+
+// Sum of the K-slice partial results in a fixed order (deterministic).
+template <int YDT>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int splits,
+                                                         int64_t mn, void* y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float v = part[i];
+  for (int s = 1; s < splits; ++s) v += part[(int64_t)s * mn + i];
+  store_y<YDT>(y, i, v);
 }
 
 // Dynamic LDS bytes of one stream_kernel workgroup.
@@ -573,6 +607,177 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
       }
 }
 
+// INT4 weights x fp16 activations GEMM (m > 16, prefill).  Workgroup tile
+// 128 (m) x 256 (n), 8 waves as 2 (m) x 4 (n), each wave 64 x 64 = 4 x 4 MFMA
+// tiles of 16x16; K advances one group (128) per step.
+//
+//  * Activations: the workgroup's 128 x 128 slice of x for a group is staged
+//    into a 3-deep LDS ring with direct global->LDS loads (chunk c16 of row r
+//    at slot c16 ^ (r & 15): conflict-free operand reads), so one barrier
+//    per group suffices: it publishes group g's slice and proves every wave
+//    is done with the buffer that group g+2 then refills.
+//  * Codes never pass through LDS: each wave loads the 16-byte chunks of its
+//    own 64 rows straight into registers (3 groups in flight) and dequantizes
+//    them exactly into MFMA operands: the exponent-bias unpack gives 1024 + q
+//    in fp16, a packed fp16 add of -(1024 + z) gives q - z exactly, and a
+//    packed fp16 multiply by the scale gives (q - z) * s rounded once -- the
+//    same 16-bit weight the dequantization defines.  The activations are
+//    permuted to the unpack's pair order on the way out of LDS.
+//  * The workgroup's scales and zero points (contiguous for its 256 rows)
+//    are staged into LDS once.
+// Staged scale / zero-point capacity of gemm_i4_kernel: 256 rows x up to
+// kGemmMaxGroups groups (K <= 12288).
+constexpr int kGemmMaxGroups = 96;
+constexpr int kGemmScaleBytes = 256 * kGemmMaxGroups * 2;
+constexpr int kGemmZeroBytes = 256 * kGemmMaxGroups / 2;
+
+template <int YDT>
+__global__ __launch_bounds__(512) void gemm_i4_kernel(GemmArgs a) {
+  constexpr int NW = 8, BM = 128, BN = 256;
+  constexpr int XBUF = BM * 16;                  // 16-byte chunks per ring buffer
+  constexpr int XI = XBUF / 64 / NW;             // direct loads per wave and group
+  constexpr int WU = 4;                          // code loads per wave and group
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  // three separate arrays, so the compiler can tell the buffer being read
+  // from the one being refilled and waits only for the loads that fill it
+  __shared__ uint4_t xr0[XBUF], xr1[XBUF], xr2[XBUF];
+  // staged scales and zero points (static too, for the same reason)
+  __shared__ __attribute__((aligned(16))) uint8_t scl[kGemmScaleBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t zcl[kGemmZeroBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int nl = lane & 15, kq = lane >> 4;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int G = a.G;
+  const int SCB = (BN * G * 2 + 1023) / 1024 * 1024;
+  const int ZCB = (BN * a.zb + 1023) / 1024 * 1024;
+
+  // staged scales and zero points of rows n0 .. n0+255 (clamped at the end
+  // of the buffers; rows past n are never stored)
+  {
+    const int nsc = SCB / 1024, nzc = ZCB / 1024;
+    const int64_t sbytes = (int64_t)a.n * G * 2, zbytes = (int64_t)a.n * a.zb;
+    for (int i = wave; i < nsc + nzc; i += NW) {
+      const bool isz = i >= nsc;
+      const int j = isz ? i - nsc : i;
+      const int64_t off = (int64_t)n0 * (isz ? a.zb : 2 * G) + j * 1024 + lane * 16;
+      const uint8_t* src = (isz ? a.zeros : static_cast<const uint8_t*>(a.scales)) +
+                           min(off, (isz ? zbytes : sbytes) - 16);
+      lds_dma16(src, (lds_void_t*)((isz ? zcl : scl) + j * 1024));
+    }
+    asm volatile("" ::: "memory");
+  }
+
+  const uint4_t* q4 = reinterpret_cast<const uint4_t*>(a.codes);
+  const int k32 = a.k / 32;
+  uint4_t wv[3][4];
+  // loads of group g (clamped: groups past the end reload the last one, so
+  // every step issues the same number of loads and the compiler's wait
+  // counts stay exact)
+  auto issue = [&](int gi, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    const int g = min(gi, G - 1);
+    uint4_t* buf = b == 0 ? xr0 : (b == 1 ? xr1 : xr2);
+#pragma unroll
+    for (int t = 0; t < XI; ++t) {
+      const int i = t * NW + wave;                // wave-uniform
+      const int sl = i * 64 + lane;
+      const int r = sl >> 4;
+      const int c16 = (sl & 15) ^ (r & 15);
+      const int row = min(m0 + r, a.m - 1);
+      lds_dma16(a.x + (int64_t)row * a.k + g * 128 + c16 * 8, (lds_void_t*)(buf + i * 64));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = min(n0 + wn * 64 + j * 16 + nl, a.n - 1);
+      wv[b][j] = q4[(int64_t)row * k32 + g * 4 + kq];
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  float4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, std::integral_constant<int, 0>{});
+  issue(1, std::integral_constant<int, 1>{});
+
+  auto step = [&](int g, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    vm_wait<WU + XI + WU>();                       // this wave's slice of group g landed
+    wg_barrier();                                  // ... every wave's; buffer b+2 is free
+    issue(g + 2, std::integral_constant<int, (b + 2) % 3>{});
+    // scales and zero points of this wave's 4 row tiles for group g
+    half2_t s2[4], nz2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 64 + j * 16 + nl;
+      _Float16 sc;
+      __builtin_memcpy(&sc, scl + (r * G + g) * 2, 2);
+      const uint32_t zb = zcl[r * a.zb + (g >> 1)];
+      const _Float16 nz = (_Float16)(-(1024.0f + (float)((g & 1) ? (zb >> 4) : (zb & 15u))));
+      s2[j] = half2_t{sc, sc};
+      nz2[j] = half2_t{nz, nz};
+    }
+    const uint4_t* buf = b == 0 ? xr0 : (b == 1 ? xr1 : xr2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4_t A[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + i * 16 + nl;
+        A[i] = perm_x(buf[r * 16 + ((kq * 4 + s) ^ nl)]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4_t u = unpack_biased_f16(wv[b][j][s]);
+        uint4_t B;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // through scalar copies: a bit_cast straight from the vector
+          // element produced wrong code here
+          const uint32_t ue = u[e];
+          half2_t h;
+          __builtin_memcpy(&h, &ue, 4);
+          h = (h + nz2[j]) * s2[j];
+          uint32_t be;
+          __builtin_memcpy(&be, &h, 4);
+          B[e] = be;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16<WQ_F16>(A[i], B, acc[i][j]);
+      }
+    }
+  };
+  for (int g0 = 0; g0 < G; g0 += 3) {
+    [&]<int... B>(std::integer_sequence<int, B...>) {
+      ((g0 + B < G ? step(g0 + B, std::integral_constant<int, B>{}) : void()), ...);
+    }(std::make_integer_sequence<int, 3>{});
+  }
+  vm_wait<0>();   // the clamped loads past the last group
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int mm = m0 + wm * 64 + i * 16 + kq * 4 + e;
+        const int nn = n0 + wn * 64 + j * 16 + nl;
+        if (mm < a.m && nn < a.n) store_y<YDT>(a.y, (int64_t)mm * a.n + nn, acc[i][j][e]);
+      }
+}
+
+template <int YDT>
+hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)((a.m + 127) / 128));
+  gemm_i4_kernel<YDT><<<grid, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launch
 // Streaming decode configurations: NW, TPG, GPP, MP, NBUF.
 template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL>
@@ -591,7 +796,13 @@ hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& 
     while (lds > cur && !allowed.compare_exchange_weak(cur, lds)) {
     }
   }
-  kern<<<dim3((unsigned)p.grid), NW * 64, lds, s>>>(a, lv, p.phases);
+  kern<<<dim3((unsigned)p.grid, (unsigned)p.splits), NW * 64, lds, s>>>(a, lv, p.phases,
+                                                                         p.kslice);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t mn = (int64_t)a.m * a.n;
+  splitk_sum_kernel<YDT><<<dim3((unsigned)((mn + 255) / 256)), 256, 0, s>>>(a.partial, p.splits,
+                                                                            mn, a.y);
   return hipGetLastError();
 }
 
@@ -619,6 +830,22 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
     WQ_STR(32, 4, 1, 1, 16, 4)
     WQ_STR(33, 4, 1, 4, 1, 4)
     WQ_STR(34, 8, 1, 2, 1, 4)
+    WQ_STR(40, 8, 1, 1, 1, 2)
+    WQ_STR(41, 8, 1, 1, 1, 3)
+    WQ_STR(42, 8, 1, 1, 4, 2)
+    WQ_STR(43, 8, 3, 1, 16, 2)
+    WQ_STR(44, 8, 3, 1, 16, 3)
+    WQ_STR(45, 8, 1, 1, 16, 2)
+    WQ_STR(46, 8, 1, 1, 16, 3)
+    WQ_STR(47, 8, 1, 2, 1, 2)
+    WQ_STR(48, 4, 3, 1, 16, 2)
+    WQ_STR(49, 4, 3, 1, 16, 3)
+    WQ_STR(50, 8, 2, 1, 16, 2)
+    WQ_STR(51, 8, 4, 1, 16, 2)
+    WQ_STR(52, 8, 6, 1, 16, 2)
+    WQ_STR(53, 8, 4, 1, 16, 3)
+    WQ_STR(54, 8, 2, 1, 4, 2)
+    WQ_STR(55, 8, 2, 2, 1, 2)
     default: return hipErrorInvalidConfiguration;
   }
 #undef WQ_STR
@@ -642,6 +869,8 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
     a.G = (int)(w->k / 128);
     a.zb = (a.G + 1) / 2;
     a.y = y;
+    if (XDT == WQ_F16 && w->fmt == WQ_FMT_INT4_ASYM && p.szl && a.G <= kGemmMaxGroups)
+      return launch_gemm_i4<YDT>(a, s);
     const dim3 grid((unsigned)((w->n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
     if (w->fmt == WQ_FMT_NF4)
       gemm_kernel<WQ_FMT_NF4, XDT, YDT><<<grid, 256, 0, s>>>(a, lv);
@@ -661,7 +890,7 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
   a.G = (int)(w->k / 128);
   a.zb = (a.G + 1) / 2;
   a.y = y;
-  (void)ws;
+  a.partial = static_cast<float*>(ws);
   return w->fmt == WQ_FMT_NF4 ? launch_stream<XDT, YDT, WQ_FMT_NF4>(a, lv, p, s)
                               : launch_stream<XDT, YDT, WQ_FMT_INT4_ASYM>(a, lv, p, s);
 }
@@ -680,18 +909,24 @@ hipError_t launch_x(const void* x, int64_t m, const wq_weight* w, const float* l
 
 W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   // Streaming decode configurations (NW waves, TPG row tiles, GPP groups per
-  // wave and phase, MP staged activation rows); NBUF is 4 except for cfg 20.
-  struct SCfg { int id, nw, tpg, gpp, mp; };
+  // wave and phase, MP staged activation rows, NBUF phases in flight).
+  struct SCfg { int id, nw, tpg, gpp, mp, nbuf; };
   static const SCfg scfgs[] = {
-      {20, 4, 1, 4, 1}, {21, 4, 1, 2, 1}, {22, 8, 1, 1, 1}, {23, 4, 2, 2, 1}, {24, 4, 1, 1, 4},
-      {25, 8, 1, 1, 4}, {26, 4, 2, 1, 4}, {27, 8, 3, 1, 16}, {28, 4, 3, 1, 16}, {29, 8, 1, 1, 16},
-      {30, 4, 2, 1, 16}, {31, 8, 2, 1, 16}, {32, 4, 1, 1, 16}, {33, 4, 1, 4, 1}, {34, 8, 1, 2, 1}};
+      {20, 4, 1, 4, 1, 2},  {21, 4, 1, 2, 1, 4},  {22, 8, 1, 1, 1, 4},  {23, 4, 2, 2, 1, 4},
+      {24, 4, 1, 1, 4, 4},  {25, 8, 1, 1, 4, 4},  {26, 4, 2, 1, 4, 4},  {27, 8, 3, 1, 16, 4},
+      {28, 4, 3, 1, 16, 4}, {29, 8, 1, 1, 16, 4}, {30, 4, 2, 1, 16, 4}, {31, 8, 2, 1, 16, 4},
+      {32, 4, 1, 1, 16, 4}, {33, 4, 1, 4, 1, 4},  {34, 8, 1, 2, 1, 4},  {40, 8, 1, 1, 1, 2},
+      {41, 8, 1, 1, 1, 3},  {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2}, {44, 8, 3, 1, 16, 3},
+      {45, 8, 1, 1, 16, 2}, {46, 8, 1, 1, 16, 3}, {47, 8, 1, 2, 1, 2},  {48, 4, 3, 1, 16, 2},
+      {49, 4, 3, 1, 16, 3}, {50, 8, 2, 1, 16, 2}, {51, 8, 4, 1, 16, 2}, {52, 8, 6, 1, 16, 2},
+      {53, 8, 4, 1, 16, 3}, {54, 8, 2, 1, 4, 2},  {55, 8, 2, 2, 1, 2}};
   W4Plan p;
   p.path = m > 16 ? 1 : 3;
   p.tpg = 1;
   p.gpw = 1;
   p.mp = 1;
   p.splits = 1;
+  p.kslice = 0;
   p.cfg = 0;
   p.phases = 1;
   p.grid = 0;
@@ -702,26 +937,36 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   if (p.path == 1) return p;
   const int64_t G = w->k / 128;
   const int64_t ntiles = (w->n + 15) / 16;
-  // measured on MI355X (graph-replayed calls of the 7B/8B decode shapes):
-  //  m = 1: one group per wave and phase, two when K is long;
+  // measured on MI355X (graph-replayed calls of the 7B/8B decode shapes);
+  // two phases in flight per wave beat deeper pipelines: with every load in
+  // flight at once the memory system returns the phases out of order, and a
+  // wave's loads complete in issue order, so its multiply waits for all of
+  // them.
+  //  m = 1: eight waves, one group per wave and phase (two for long K or
+  //         many rows);
   //  m <= 4: eight waves, one tile;
-  //  m <= 16: one workgroup per CU (128 KB of activation ring), as many
-  //           tiles per workgroup as that takes (at most 3).
+  //  m <= 16: one workgroup per CU, as many tiles per workgroup as that
+  //           takes (at most 3).
   int cfg;
   if (m <= 1) {
-    cfg = G >= 64 ? 34 : 22;
+    cfg = (G >= 64 || ntiles >= 768) ? 47 : 40;
   } else if (m <= 4) {
-    cfg = 25;
+    cfg = 42;
   } else {
     const int64_t tpg = (ntiles + 255) / 256;
-    cfg = tpg >= 3 ? 27 : (tpg == 2 ? 31 : 29);
+    cfg = tpg >= 3 ? 43 : (tpg == 2 ? 50 : 45);
   }
+  int splits = 1;
 #ifdef WQ_TUNE_ENV
   if (const char* e = getenv("WQ_DECODE")) {
     int c = -1;
     if (sscanf(e, "%d", &c) == 1)
       for (const SCfg& sc : scfgs)
         if (sc.id == c) cfg = c;
+  }
+  if (const char* e = getenv("WQ_SPLIT")) {
+    int v = 0;
+    if (sscanf(e, "%d", &v) == 1 && v >= 1 && v <= 16) splits = v;
   }
 #endif
   for (const SCfg& sc : scfgs)
@@ -730,11 +975,15 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
       p.tpg = sc.tpg;
       p.gpw = sc.gpp;
       p.mp = sc.mp;
-      p.phases = (int)((G + sc.nw * sc.gpp - 1) / (sc.nw * sc.gpp));
+      p.splits = (int)std::min<int64_t>(splits, G);
+      p.kslice = (int)((G + p.splits - 1) / p.splits);
+      p.splits = (int)((G + p.kslice - 1) / p.kslice);   // no empty slice
+      p.phases = (p.kslice + sc.nw * sc.gpp - 1) / (sc.nw * sc.gpp);
       p.grid = (int)((ntiles + sc.tpg - 1) / sc.tpg);
+      if (p.splits > 1) p.ws = (size_t)p.splits * (size_t)m * (size_t)w->n * sizeof(float);
       // staged scales must fit beside the activation ring
       if (p.szl) {
-        const size_t lds = (size_t)sc.nw * 4 * ((sc.mp * sc.gpp * 16 + 63) / 64 * 64) * 16 +
+        const size_t lds = (size_t)sc.nw * sc.nbuf * ((sc.mp * sc.gpp * 16 + 63) / 64 * 64) * 16 +
                            (size_t)sc.tpg * ((32 * G + 1023) / 1024 * 1024 +
                                              (16 * ((G + 1) / 2) + 1023) / 1024 * 1024);
         if (lds > 160 * 1024 - 256) p.szl = false;

@@ -139,6 +139,9 @@ def test_linear_skinny_parity(m, n, k, xdt, ydt):
     (130, 129, 256, "f16", "bf16"),
     (200, 520, 1024, "bf16", "f32"),
     (256, 1024, 4096, "f16", "f16"),
+    (130, 272, 1024, "f16", "f32"),   # staged-scale GEMM: ragged m and n tiles
+    (40, 4096, 4096, "f16", "bf16"),  # one partial m tile, full n tiles
+    (300, 11008, 4096, "f16", "f32"), # the up-projection rows, three m tiles
 ])
 def test_linear_gemm_parity(m, n, k, xdt, ydt):
     say(f"linear_gemm m={m} n={n} k={k} x={xdt} y={ydt}")

@@ -107,7 +107,7 @@ struct Levels {
 
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   uint32_t r;
-  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
   return r;
 }
 
@@ -608,45 +608,51 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
 }
 
 // INT4 weights x fp16 activations GEMM (m > 16, prefill).  Workgroup tile
-// 128 (m) x 256 (n), 8 waves as 2 (m) x 4 (n), each wave 64 x 64 = 4 x 4 MFMA
-// tiles of 16x16; K advances one group (128) per step.
+// 128 (m) x 256 (n), 4 waves side by side along n, each 128 x 64 = 8 x 4
+// MFMA tiles of 16x16; K advances one group (128) per step.  Every code is
+// dequantized in registers by the wave that uses it, so the vector work per
+// MFMA falls with the rows a wave covers; 128-row waves keep it under the
+// matrix-core time on gfx950 (a wave64 vector instruction issues in about 4
+// cycles, a 16x16x32 MFMA in 16).
 //
-//  * Activations: the workgroup's 128 x 128 slice of x for a group is staged
-//    into a 3-deep LDS ring with direct global->LDS loads (chunk c16 of row r
-//    at slot c16 ^ (r & 15): conflict-free operand reads), so one barrier
-//    per group suffices: it publishes group g's slice and proves every wave
-//    is done with the buffer that group g+2 then refills.
-//  * Codes never pass through LDS: each wave loads the 16-byte chunks of its
-//    own 64 rows straight into registers (3 groups in flight) and dequantizes
-//    them exactly into MFMA operands: the exponent-bias unpack gives 1024 + q
-//    in fp16, a packed fp16 add of -(1024 + z) gives q - z exactly, and a
-//    packed fp16 multiply by the scale gives (q - z) * s rounded once -- the
-//    same 16-bit weight the dequantization defines.  The activations are
-//    permuted to the unpack's pair order on the way out of LDS.
+//  * Both operands reach LDS by direct global->LDS loads, issued ahead of
+//    use: the activation slice of group g+1 (2 buffers) and the codes of
+//    group g+2 (3 buffers) during step g.  One barrier per step publishes
+//    group g's buffers and proves every wave is done with the ones being
+//    refilled.  No load lands in a register inside the loop, so the
+//    compiler adds no waits of its own; the explicit wait before the barrier
+//    counts exactly the loads issued after the ones it needs.
+//    Activation chunk c16 of row r sits at slot c16 ^ (r & 15)
+//    (conflict-free operand reads); codes are row-major, 64 bytes a row.
+//  * Codes are dequantized exactly in the natural k order: byte e of a word
+//    is copied into bytes 0 and 2 (v_perm_b32), its low nibble OR'ed into
+//    1024.0 (giving 1024 + q) and its high nibble, now at bits 4-7 of the
+//    upper half, into 64.0 (where the mantissa step is 1/16, giving 64 + q);
+//    a packed fp16 add of -(bias + z) gives q - z exactly and a packed fp16
+//    multiply by the scale gives (q - z) * s rounded once -- the 16-bit
+//    weight the dequantization defines.
 //  * The workgroup's scales and zero points (contiguous for its 256 rows)
 //    are staged into LDS once.
-// Staged scale / zero-point capacity of gemm_i4_kernel: 256 rows x up to
-// kGemmMaxGroups groups (K <= 12288).
-constexpr int kGemmMaxGroups = 96;
+// Staged scale / zero-point capacity: 256 rows x up to kGemmMaxGroups groups.
+constexpr int kGemmMaxGroups = 64;
 constexpr int kGemmScaleBytes = 256 * kGemmMaxGroups * 2;
 constexpr int kGemmZeroBytes = 256 * kGemmMaxGroups / 2;
 
 template <int YDT>
-__global__ __launch_bounds__(512) void gemm_i4_kernel(GemmArgs a) {
-  constexpr int NW = 8, BM = 128, BN = 256;
-  constexpr int XBUF = BM * 16;                  // 16-byte chunks per ring buffer
-  constexpr int XI = XBUF / 64 / NW;             // direct loads per wave and group
-  constexpr int WU = 4;                          // code loads per wave and group
+__global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
+  constexpr int NW = 4, BM = 128, BN = 256;
+  constexpr int XBUF = BM * 16;                  // 16-byte chunks per activation buffer
+  constexpr int WBUF = BN * 4;                   // 16-byte chunks per code buffer
+  constexpr int XI = XBUF / 64 / NW;             // activation loads per wave and group
+  constexpr int WI = WBUF / 64 / NW;             // code loads per wave and group
   typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-  // three separate arrays, so the compiler can tell the buffer being read
-  // from the one being refilled and waits only for the loads that fill it
-  __shared__ uint4_t xr0[XBUF], xr1[XBUF], xr2[XBUF];
-  // staged scales and zero points (static too, for the same reason)
+  __shared__ uint4_t xr[2 * XBUF];
+  __shared__ uint4_t wr[3 * WBUF];
   __shared__ __attribute__((aligned(16))) uint8_t scl[kGemmScaleBytes];
   __shared__ __attribute__((aligned(16))) uint8_t zcl[kGemmZeroBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wn = wave;
   const int nl = lane & 15, kq = lane >> 4;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int G = a.G;
@@ -666,106 +672,113 @@ __global__ __launch_bounds__(512) void gemm_i4_kernel(GemmArgs a) {
                            min(off, (isz ? zbytes : sbytes) - 16);
       lds_dma16(src, (lds_void_t*)((isz ? zcl : scl) + j * 1024));
     }
-    asm volatile("" ::: "memory");
   }
 
-  const uint4_t* q4 = reinterpret_cast<const uint4_t*>(a.codes);
-  const int k32 = a.k / 32;
-  uint4_t wv[3][4];
-  // loads of group g (clamped: groups past the end reload the last one, so
-  // every step issues the same number of loads and the compiler's wait
-  // counts stay exact)
-  auto issue = [&](int gi, auto bc) {
-    constexpr int b = decltype(bc)::value;
-    const int g = min(gi, G - 1);
-    uint4_t* buf = b == 0 ? xr0 : (b == 1 ? xr1 : xr2);
+  // per-lane source offsets of the direct loads (a group adds a uniform one)
+  const char* const xb = reinterpret_cast<const char*>(a.x);
+  const char* const cb = reinterpret_cast<const char*>(a.codes);
+  uint32_t xoff[XI], woff[WI];
 #pragma unroll
-    for (int t = 0; t < XI; ++t) {
-      const int i = t * NW + wave;                // wave-uniform
-      const int sl = i * 64 + lane;
-      const int r = sl >> 4;
-      const int c16 = (sl & 15) ^ (r & 15);
-      const int row = min(m0 + r, a.m - 1);
-      lds_dma16(a.x + (int64_t)row * a.k + g * 128 + c16 * 8, (lds_void_t*)(buf + i * 64));
-    }
+  for (int t = 0; t < XI; ++t) {
+    const int i = t * NW + wave;                 // load i fills slots 64 i .. 64 i + 63
+    const int r = i * 4 + (lane >> 4);
+    const int c16 = (lane & 15) ^ (r & 15);
+    xoff[t] = (uint32_t)(min(m0 + r, a.m - 1) * a.k * 2 + c16 * 16);
+  }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = min(n0 + wn * 64 + j * 16 + nl, a.n - 1);
-      wv[b][j] = q4[(int64_t)row * k32 + g * 4 + kq];
-    }
-    asm volatile("" ::: "memory");
+  for (int t = 0; t < WI; ++t) {
+    const int i = t * NW + wave;
+    const int row = i * 16 + (lane >> 2);
+    woff[t] = (uint32_t)(min(n0 + row, a.n - 1) * (a.k / 2) + (lane & 3) * 16);
+  }
+  // direct loads of group g (clamped: groups past the end reload the last
+  // one, so every step issues the same loads)
+  auto issue_x = [&](int gi) {
+    const char* base = xb + (int64_t)min(gi, G - 1) * 256;
+    uint4_t* buf = xr + (gi & 1) * XBUF;
+#pragma unroll
+    for (int t = 0; t < XI; ++t) lds_dma16(base + xoff[t], (lds_void_t*)(buf + (t * NW + wave) * 64));
+  };
+  auto issue_w = [&](int gi) {
+    const char* base = cb + (int64_t)min(gi, G - 1) * 64;
+    uint4_t* buf = wr + (gi % 3) * WBUF;
+#pragma unroll
+    for (int t = 0; t < WI; ++t) lds_dma16(base + woff[t], (lds_void_t*)(buf + (t * NW + wave) * 64));
   };
 
-  float4_t acc[4][4];
+  float4_t acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, std::integral_constant<int, 0>{});
-  issue(1, std::integral_constant<int, 1>{});
+  issue_w(0);
+  issue_x(0);
+  issue_w(1);
 
-  auto step = [&](int g, auto bc) {
-    constexpr int b = decltype(bc)::value;
-    vm_wait<WU + XI + WU>();                       // this wave's slice of group g landed
-    wg_barrier();                                  // ... every wave's; buffer b+2 is free
-    issue(g + 2, std::integral_constant<int, (b + 2) % 3>{});
-    // scales and zero points of this wave's 4 row tiles for group g
+  constexpr uint32_t kMask = 0x00F0000Fu, kBias = 0x54006400u;   // 64.0 (hi), 1024.0 (lo)
+  for (int g = 0; g < G; ++g) {
+    // this wave's loads of group g's activations (and, issued earlier, its
+    // codes and the staged scales) have landed: only the codes of group g+1
+    // were issued after them
+    vm_wait<WI>();
+    wg_barrier();   // ... and every wave's; the buffers refilled below are free
+    issue_x(g + 1);
+    issue_w(g + 2);
+    const uint4_t* xcur = xr + (g & 1) * XBUF;
+    const uint4_t* wcur = wr + (g % 3) * WBUF;
+    // codes, scales and zero points of this wave's 4 row tiles for group g
+    uint4_t wv[4];
     half2_t s2[4], nz2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 64 + j * 16 + nl;
-      _Float16 sc;
-      __builtin_memcpy(&sc, scl + (r * G + g) * 2, 2);
+      wv[j] = wcur[r * 4 + kq];
+      _Float16 sc16;
+      __builtin_memcpy(&sc16, scl + (r * G + g) * 2, 2);
       const uint32_t zb = zcl[r * a.zb + (g >> 1)];
-      const _Float16 nz = (_Float16)(-(1024.0f + (float)((g & 1) ? (zb >> 4) : (zb & 15u))));
-      s2[j] = half2_t{sc, sc};
-      nz2[j] = half2_t{nz, nz};
+      const float z = (float)((g & 1) ? (zb >> 4) : (zb & 15u));
+      s2[j] = half2_t{sc16, sc16};
+      nz2[j] = half2_t{(_Float16)(-(1024.0f + z)), (_Float16)(-(64.0f + z))};
     }
-    const uint4_t* buf = b == 0 ? xr0 : (b == 1 ? xr1 : xr2);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4_t A[4];
+      uint4_t A[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + nl;
-        A[i] = perm_x(buf[r * 16 + ((kq * 4 + s) ^ nl)]);
+      for (int i = 0; i < 8; ++i) {
+        const int r = i * 16 + nl;
+        A[i] = xcur[r * 16 + ((kq * 4 + s) ^ nl)];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint4_t u = unpack_biased_f16(wv[b][j][s]);
+        const uint32_t w = wv[j][s];
         uint4_t B;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // through scalar copies: a bit_cast straight from the vector
-          // element produced wrong code here
-          const uint32_t ue = u[e];
+          const uint32_t u = and_or(__builtin_amdgcn_perm(w, w, 0x01010101u * e), kMask, kBias);
+          // through scalar copies: a bit_cast straight from a vector element
+          // produced wrong code here
           half2_t h;
-          __builtin_memcpy(&h, &ue, 4);
+          __builtin_memcpy(&h, &u, 4);
           h = (h + nz2[j]) * s2[j];
           uint32_t be;
           __builtin_memcpy(&be, &h, 4);
           B[e] = be;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16<WQ_F16>(A[i], B, acc[i][j]);
+        for (int i = 0; i < 8; ++i) acc[i][j] = mfma16<WQ_F16>(A[i], B, acc[i][j]);
       }
     }
-  };
-  for (int g0 = 0; g0 < G; g0 += 3) {
-    [&]<int... B>(std::integer_sequence<int, B...>) {
-      ((g0 + B < G ? step(g0 + B, std::integral_constant<int, B>{}) : void()), ...);
-    }(std::make_integer_sequence<int, 3>{});
   }
   vm_wait<0>();   // the clamped loads past the last group
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int mm = m0 + wm * 64 + i * 16 + kq * 4 + e;
+        const int mm = m0 + i * 16 + kq * 4 + e;
         const int nn = n0 + wn * 64 + j * 16 + nl;
         if (mm < a.m && nn < a.n) store_y<YDT>(a.y, (int64_t)mm * a.n + nn, acc[i][j][e]);
       }
@@ -774,7 +787,7 @@ __global__ __launch_bounds__(512) void gemm_i4_kernel(GemmArgs a) {
 template <int YDT>
 hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)((a.m + 127) / 128));
-  gemm_i4_kernel<YDT><<<grid, 512, 0, s>>>(a);
+  gemm_i4_kernel<YDT><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -622,8 +622,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
 //    refilled.  No load lands in a register inside the loop, so the
 //    compiler adds no waits of its own; the explicit wait before the barrier
 //    counts exactly the loads issued after the ones it needs.
-//    Activation chunk c16 of row r sits at slot c16 ^ (r & 15)
-//    (conflict-free operand reads); codes are row-major, 64 bytes a row.
+//    Activation chunk c16 of row r sits at slot c16 ^ (r & 15), code chunk c
+//    (of 4) of row r at slot c ^ ((r >> 2) & 3): conflict-free operand reads.
 //  * Codes are dequantized exactly in the natural k order: byte e of a word
 //    is copied into bytes 0 and 2 (v_perm_b32), its low nibble OR'ed into
 //    1024.0 (giving 1024 + q) and its high nibble, now at bits 4-7 of the
@@ -635,12 +635,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
 //    are staged into LDS once.
 // Staged scale / zero-point capacity: 256 rows x up to kGemmMaxGroups groups.
 constexpr int kGemmMaxGroups = 64;
+#ifndef WQ_GEMM_WAVES
+#define WQ_GEMM_WAVES 8
+#endif
+constexpr int kGemmWaves = WQ_GEMM_WAVES;   // 4: 128 x 64 per wave; 8: 128 x 32
 constexpr int kGemmScaleBytes = 256 * kGemmMaxGroups * 2;
 constexpr int kGemmZeroBytes = 256 * kGemmMaxGroups / 2;
 
-template <int YDT>
-__global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
-  constexpr int NW = 4, BM = 128, BN = 256;
+template <int YDT, int NWG>
+__global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
+  constexpr int NW = NWG, BM = 128, BN = 256;
+  constexpr int NF = BN / 16 / NW;               // 16-row code tiles per wave (n)
   constexpr int XBUF = BM * 16;                  // 16-byte chunks per activation buffer
   constexpr int WBUF = BN * 4;                   // 16-byte chunks per code buffer
   constexpr int XI = XBUF / 64 / NW;             // activation loads per wave and group
@@ -652,7 +657,7 @@ __global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t zcl[kGemmZeroBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave;
+  const int wn = wave;                           // the wave's rows: wn * 16 * NF + [0, 16 * NF)
   const int nl = lane & 15, kq = lane >> 4;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int G = a.G;
@@ -689,7 +694,8 @@ __global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
   for (int t = 0; t < WI; ++t) {
     const int i = t * NW + wave;
     const int row = i * 16 + (lane >> 2);
-    woff[t] = (uint32_t)(min(n0 + row, a.n - 1) * (a.k / 2) + (lane & 3) * 16);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);   // chunk c of a row sits at slot c ^ ((row >> 2) & 3)
+    woff[t] = (uint32_t)(min(n0 + row, a.n - 1) * (a.k / 2) + c * 16);
   }
   // direct loads of group g (clamped: groups past the end reload the last
   // one, so every step issues the same loads)
@@ -706,11 +712,11 @@ __global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
     for (int t = 0; t < WI; ++t) lds_dma16(base + woff[t], (lds_void_t*)(buf + (t * NW + wave) * 64));
   };
 
-  float4_t acc[8][4];
+  float4_t acc[8][NF];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NF; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   issue_w(0);
   issue_x(0);
@@ -728,12 +734,12 @@ __global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
     const uint4_t* xcur = xr + (g & 1) * XBUF;
     const uint4_t* wcur = wr + (g % 3) * WBUF;
     // codes, scales and zero points of this wave's 4 row tiles for group g
-    uint4_t wv[4];
-    half2_t s2[4], nz2[4];
+    uint4_t wv[NF];
+    half2_t s2[NF], nz2[NF];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 64 + j * 16 + nl;
-      wv[j] = wcur[r * 4 + kq];
+    for (int j = 0; j < NF; ++j) {
+      const int r = wn * 16 * NF + j * 16 + nl;
+      wv[j] = wcur[r * 4 + (kq ^ ((r >> 2) & 3))];
       _Float16 sc16;
       __builtin_memcpy(&sc16, scl + (r * G + g) * 2, 2);
       const uint32_t zb = zcl[r * a.zb + (g >> 1)];
@@ -745,12 +751,9 @@ __global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
     for (int s = 0; s < 4; ++s) {
       uint4_t A[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = i * 16 + nl;
-        A[i] = xcur[r * 16 + ((kq * 4 + s) ^ nl)];
-      }
+      for (int i = 0; i < 8; ++i) A[i] = xcur[(i * 16 + nl) * 16 + ((kq * 4 + s) ^ nl)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NF; ++j) {
         const uint32_t w = wv[j][s];
         uint4_t B;
 #pragma unroll
@@ -775,11 +778,11 @@ __global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NF; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int mm = m0 + i * 16 + kq * 4 + e;
-        const int nn = n0 + wn * 64 + j * 16 + nl;
+        const int nn = n0 + wn * 16 * NF + j * 16 + nl;
         if (mm < a.m && nn < a.n) store_y<YDT>(a.y, (int64_t)mm * a.n + nn, acc[i][j][e]);
       }
 }
@@ -787,7 +790,8 @@ __global__ __launch_bounds__(256) void gemm_i4_kernel(GemmArgs a) {
 template <int YDT>
 hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)((a.m + 127) / 128));
-  gemm_i4_kernel<YDT><<<grid, 256, 0, s>>>(a);
+  constexpr int NWG = kGemmWaves;
+  gemm_i4_kernel<YDT, NWG><<<grid, NWG * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -394,10 +394,16 @@ def summarize_pmc(fetch_csv, write_csv, kernel_substr, copy_mib, out_path, comma
     import csv
     import statistics
 
+    # "NAME@THREADS" selects the dispatches of NAME whose grid has THREADS
+    # work-items (one instantiation can serve several layer shapes)
+    name_substr, _, grid = kernel_substr.partition("@")
+
     def per_dispatch(path, counter):
         rows = {}
         for r in csv.DictReader(open(path)):
             if r.get("Counter_Name") != counter:
+                continue
+            if grid and name_substr in r["Kernel_Name"] and r["Grid_Size"] != grid:
                 continue
             rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return rows
@@ -409,11 +415,11 @@ def summarize_pmc(fetch_csv, write_csv, kernel_substr, copy_mib, out_path, comma
                 for v in vs]
         copy = sorted(copy)[-5:]                  # the five probe copies (largest dispatches)
         factor = statistics.median(copy) / (copy_mib * 1024.0)   # counter units per KiB moved
-        kern = [v for k, vs in rows.items() if kernel_substr in k for v in vs]
+        kern = [v for k, vs in rows.items() if name_substr in k for v in vs]
         res[counter] = (statistics.mean(kern) / factor * 1024.0, factor, len(kern))
     fetch, write = res["FETCH_SIZE"][0], res["WRITE_SIZE"][0]
-    src = os.path.join(ROOT, KERNEL_SOURCES["stream" if "stream" in kernel_substr else
-                                            ("int8" if "int8" in kernel_substr else "gemm")])
+    src = os.path.join(ROOT, KERNEL_SOURCES["stream" if "stream" in name_substr else
+                                            ("int8" if "int8" in name_substr else "gemm")])
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     with open(out_path, "w") as f:
         f.write(f"# HBM traffic of one launch of the kernels matching '{kernel_substr}',\n")
@@ -431,7 +437,46 @@ def summarize_pmc(fetch_csv, write_csv, kernel_substr, copy_mib, out_path, comma
     print(open(out_path).read())
 
 
+def summarize_trace(prof_dir, bench_json, title, out_path, command):
+    """Write a rocprofv3 --kernel-trace --stats summary: per kernel and
+    launch grid (one grid per layer shape), the calls and the average /
+    min / max duration of the dispatches, with the bench line of the same
+    run."""
+    import csv
+    import statistics
+    per = {}
+    for r in csv.DictReader(open(os.path.join(prof_dir, "run_kernel_trace.csv"))):
+        grid = tuple(int(r[f"Grid_Size_{a}"]) // max(1, int(r[f"Workgroup_Size_{a}"]))
+                     for a in "XYZ")
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        per.setdefault((r["Kernel_Name"], grid), []).append(dur)
+    total = sum(sum(v) for v in per.values())
+    rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
+    with open(out_path, "w") as f:
+        f.write(f"# rocprofv3 kernel-trace summary: {title}\n")
+        f.write("# command (repository root, on one MI355X):\n")
+        f.write(f"#   {command}\n")
+        f.write("# columns: calls, average ns, min ns, max ns, share of GPU time, "
+                "workgroups (x,y,z), kernel\n")
+        for (name, grid), v in rows:
+            f.write(f"{len(v):6d} {statistics.mean(v):12.1f} {min(v):9d} {max(v):9d} "
+                    f"{100.0 * sum(v) / total:6.2f}%  {grid}  {name[:140]}\n")
+        if bench_json and os.path.exists(bench_json):
+            d = json.load(open(bench_json))
+            rf = d.get("roofline", {})
+            f.write("\n# bench.py line of the same run (graph-replayed; kernel time from HIP events):\n")
+            f.write(f"#   value {d['value']} {d['unit']}, ms_per_step {d['ms_per_step']}, "
+                    f"dominant kernel avg_launch_us {rf.get('avg_launch_us')} "
+                    f"({rf.get('kernel')})\n")
+    print(open(out_path).read())
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        # --summarize-trace PROF_DIR BENCH_JSON TITLE OUT "COMMAND"
+        a = sys.argv[2:]
+        summarize_trace(a[0], a[1], a[2], a[3], a[4])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         # --summarize-pmc FETCH_CSV WRITE_CSV KERNEL_SUBSTR COPY_MIB OUT "COMMAND"
         a = sys.argv[2:]

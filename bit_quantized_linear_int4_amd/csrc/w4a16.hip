@@ -105,10 +105,20 @@ struct Levels {
   float v[16];
 };
 
+// c in a VGPR, opaque to the optimizer (the empty asm emits nothing).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+  asm("" : "+v"(c));
+  return c;
+}
+
+// (a & m) | o as one v_and_or_b32 / v_bitop3_b32: with m and o opaque VGPR
+// values the compiler cannot split it into two literal-operand instructions.
+// Plain C rather than inline asm on purpose: an MFMA that reads a VGPR needs
+// two wait states after the VALU instruction that wrote it, and the compiler
+// inserts them only for instructions it emitted itself, so an asm def
+// feeding an MFMA operand can be read stale.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
+  return (a & in_vgpr(m)) | in_vgpr(o);
 }
 
 // One 32-bit word of 8 codes -> 8 biased fp16 values 1024 + q, ordered
@@ -160,10 +170,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // outstanding load that must finish first); the kernels wait for their
 // direct loads themselves (vm_wait with counts that include them) before any
 // LDS read of the data.  No output register, so nothing is left in flight
-// behind the compiler's back but LDS bytes the explicit waits cover.
+// behind the compiler's back but LDS bytes the explicit waits cover.  The
+// s_nop is the one wait state an LDS-DMA instruction needs after a scalar
+// write of M0, which the compiler pads for its own such loads but cannot
+// see here.
 __device__ __forceinline__ void lds_dma16(const void* gaddr, lds_void_t* lds) {
   const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(l) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(l) : "memory");
 }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima, i.e. no wait).
@@ -205,7 +218,8 @@ __device__ __forceinline__ void vm_wait_n(int n) { vm_wait_range<0, 63>(n); }
 // for all TPG tiles, so no data is shared between the waves until the final
 // sum.  Each wave stages the activations of its own groups (MP rows, padded)
 // into a private LDS ring of NBUF phase buffers with direct global->LDS
-// loads, and keeps the codes of NBUF phases in registers.  Loads are issued
+// loads; the codes of NBUF phases are held in registers (or, with SZL, in a
+// second per-wave LDS ring filled the same way).  Loads are issued
 // phase by phase (codes, then activations), NBUF phases ahead of the
 // multiply, so the multiply of a phase starts as soon as that phase's own
 // loads have landed and the loads of later phases keep streaming meanwhile.
@@ -243,6 +257,10 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   const int ZCB = (16 * a.zb + 1023) / 1024 * 1024;
   uint8_t* const scl = reinterpret_cast<uint8_t*>(dsm + NW * NBUF * XS);
   uint8_t* const zcl = scl + TPG * SCB;
+  // SZL: the codes also arrive through LDS (per-wave ring, 1 KB per unit:
+  // lane l's 16 bytes at slot l), so no load inside the loop lands in a
+  // register and the compiler adds no waits of its own
+  uint4_t* const wring = reinterpret_cast<uint4_t*>(zcl + TPG * ZCB) + wave * NBUF * TPG * GPP * 64;
 
   if constexpr (FMT == WQ_FMT_NF4) {
     if (tid < 16) lut[tid] = lv.v[tid];
@@ -304,7 +322,12 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
 #pragma unroll
       for (int u = 0; u < GPP; ++u) {
         const int g = min(gbeg + p * CG + wave * GPP + u, a.G - 1);
-        wv[b][t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
+        if constexpr (SZL) {
+          lds_dma16(q4 + (int64_t)row * k32 + g * 4 + kq,
+                    (lds_void_t*)(wring + ((b * TPG + t) * GPP + u) * 64));
+        } else {
+          wv[b][t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
+        }
         if constexpr (SZL) {
         } else if constexpr (FMT == WQ_FMT_INT4_ASYM) {
           sv[b][t][u] = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)row * a.G + g]);
@@ -355,6 +378,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
         if constexpr (SZL) {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
+            wv[b][t][u] = wring[((b * TPG + t) * GPP + u) * 64 + lane];
             const uint16_t sc = *reinterpret_cast<const uint16_t*>(scl + t * SCB + (nl * a.G + g) * 2);
             sv[b][t][u] = f16_bits_to_f32(sc);
             zv[b][t][u] = zcl[t * ZCB + nl * a.zb + (g >> 1)];
@@ -455,7 +479,9 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
 inline size_t stream_lds_bytes(int nw, int tpg, int gpp, int mp, int nbuf, bool szl, int G, int zb) {
   const size_t xs = (size_t)((mp * gpp * 16 + 63) / 64 * 64) * 16;
   size_t b = (size_t)nw * nbuf * xs;
-  if (szl) b += (size_t)tpg * ((32 * G + 1023) / 1024 * 1024 + (16 * zb + 1023) / 1024 * 1024);
+  if (szl)
+    b += (size_t)tpg * ((32 * G + 1023) / 1024 * 1024 + (16 * zb + 1023) / 1024 * 1024) +
+         (size_t)nw * nbuf * tpg * gpp * 1024;
   const size_t red = (size_t)nw * tpg * 4 * 64 * 4;
   return b > red ? b : red;
 }
@@ -801,6 +827,7 @@ template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF,
 hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
   auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL>;
   const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, a.G, a.zb);
+  if (a.m > MP) return hipErrorInvalidValue;   // rows past MP are never staged
   if (lds > 160 * 1024 - 256) return hipErrorInvalidConfiguration;
   // raise the dynamic LDS limit of this instantiation when a launch needs
   // more than the default (the static NF4 table shares the 160 KB)
@@ -832,21 +859,8 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
     }                                                                                      \
     return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false>(a, lv, p, s);
   switch (p.cfg) {
-    WQ_STR(20, 4, 1, 4, 1, 2)
-    WQ_STR(21, 4, 1, 2, 1, 4)
     WQ_STR(22, 8, 1, 1, 1, 4)
-    WQ_STR(23, 4, 2, 2, 1, 4)
-    WQ_STR(24, 4, 1, 1, 4, 4)
-    WQ_STR(25, 8, 1, 1, 4, 4)
-    WQ_STR(26, 4, 2, 1, 4, 4)
     WQ_STR(27, 8, 3, 1, 16, 4)
-    WQ_STR(28, 4, 3, 1, 16, 4)
-    WQ_STR(29, 8, 1, 1, 16, 4)
-    WQ_STR(30, 4, 2, 1, 16, 4)
-    WQ_STR(31, 8, 2, 1, 16, 4)
-    WQ_STR(32, 4, 1, 1, 16, 4)
-    WQ_STR(33, 4, 1, 4, 1, 4)
-    WQ_STR(34, 8, 1, 2, 1, 4)
     WQ_STR(40, 8, 1, 1, 1, 2)
     WQ_STR(41, 8, 1, 1, 1, 3)
     WQ_STR(42, 8, 1, 1, 4, 2)
@@ -855,14 +869,8 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
     WQ_STR(45, 8, 1, 1, 16, 2)
     WQ_STR(46, 8, 1, 1, 16, 3)
     WQ_STR(47, 8, 1, 2, 1, 2)
-    WQ_STR(48, 4, 3, 1, 16, 2)
-    WQ_STR(49, 4, 3, 1, 16, 3)
     WQ_STR(50, 8, 2, 1, 16, 2)
-    WQ_STR(51, 8, 4, 1, 16, 2)
-    WQ_STR(52, 8, 6, 1, 16, 2)
-    WQ_STR(53, 8, 4, 1, 16, 3)
     WQ_STR(54, 8, 2, 1, 4, 2)
-    WQ_STR(55, 8, 2, 2, 1, 2)
     default: return hipErrorInvalidConfiguration;
   }
 #undef WQ_STR
@@ -929,14 +937,9 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   // wave and phase, MP staged activation rows, NBUF phases in flight).
   struct SCfg { int id, nw, tpg, gpp, mp, nbuf; };
   static const SCfg scfgs[] = {
-      {20, 4, 1, 4, 1, 2},  {21, 4, 1, 2, 1, 4},  {22, 8, 1, 1, 1, 4},  {23, 4, 2, 2, 1, 4},
-      {24, 4, 1, 1, 4, 4},  {25, 8, 1, 1, 4, 4},  {26, 4, 2, 1, 4, 4},  {27, 8, 3, 1, 16, 4},
-      {28, 4, 3, 1, 16, 4}, {29, 8, 1, 1, 16, 4}, {30, 4, 2, 1, 16, 4}, {31, 8, 2, 1, 16, 4},
-      {32, 4, 1, 1, 16, 4}, {33, 4, 1, 4, 1, 4},  {34, 8, 1, 2, 1, 4},  {40, 8, 1, 1, 1, 2},
-      {41, 8, 1, 1, 1, 3},  {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2}, {44, 8, 3, 1, 16, 3},
-      {45, 8, 1, 1, 16, 2}, {46, 8, 1, 1, 16, 3}, {47, 8, 1, 2, 1, 2},  {48, 4, 3, 1, 16, 2},
-      {49, 4, 3, 1, 16, 3}, {50, 8, 2, 1, 16, 2}, {51, 8, 4, 1, 16, 2}, {52, 8, 6, 1, 16, 2},
-      {53, 8, 4, 1, 16, 3}, {54, 8, 2, 1, 4, 2},  {55, 8, 2, 2, 1, 2}};
+      {22, 8, 1, 1, 1, 4},  {27, 8, 3, 1, 16, 4},  {40, 8, 1, 1, 1, 2},  {41, 8, 1, 1, 1, 3},
+      {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2},  {44, 8, 3, 1, 16, 3},  {45, 8, 1, 1, 16, 2},
+      {46, 8, 1, 1, 16, 3},  {47, 8, 1, 2, 1, 2},  {50, 8, 2, 1, 16, 2},  {54, 8, 2, 1, 4, 2}};
   W4Plan p;
   p.path = m > 16 ? 1 : 3;
   p.tpg = 1;
@@ -959,14 +962,13 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   // flight at once the memory system returns the phases out of order, and a
   // wave's loads complete in issue order, so its multiply waits for all of
   // them.
-  //  m = 1: eight waves, one group per wave and phase (two for long K or
-  //         many rows);
+  //  m = 1: eight waves, one group per wave and phase (two for long K);
   //  m <= 4: eight waves, one tile;
   //  m <= 16: one workgroup per CU, as many tiles per workgroup as that
   //           takes (at most 3).
   int cfg;
   if (m <= 1) {
-    cfg = (G >= 64 || ntiles >= 768) ? 47 : 40;
+    cfg = G >= 64 ? 47 : 40;
   } else if (m <= 4) {
     cfg = 42;
   } else {
@@ -979,7 +981,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
     int c = -1;
     if (sscanf(e, "%d", &c) == 1)
       for (const SCfg& sc : scfgs)
-        if (sc.id == c) cfg = c;
+        if (sc.id == c && sc.mp >= m) cfg = c;   // a schedule stages at most mp rows
   }
   if (const char* e = getenv("WQ_SPLIT")) {
     int v = 0;
@@ -1000,9 +1002,8 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
       if (p.splits > 1) p.ws = (size_t)p.splits * (size_t)m * (size_t)w->n * sizeof(float);
       // staged scales must fit beside the activation ring
       if (p.szl) {
-        const size_t lds = (size_t)sc.nw * sc.nbuf * ((sc.mp * sc.gpp * 16 + 63) / 64 * 64) * 16 +
-                           (size_t)sc.tpg * ((32 * G + 1023) / 1024 * 1024 +
-                                             (16 * ((G + 1) / 2) + 1023) / 1024 * 1024);
+        const size_t lds = stream_lds_bytes(sc.nw, sc.tpg, sc.gpp, sc.mp, sc.nbuf, true, (int)G,
+                                            (int)((G + 1) / 2));
         if (lds > 160 * 1024 - 256) p.szl = false;
       }
     }

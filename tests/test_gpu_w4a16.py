@@ -118,6 +118,8 @@ def oracle_linear(x_np, w_np, xdt, rows=None):
     (16, 1000, 2048, "f16", "f32"),
     (16, 4096, 11008, "f16", "f32"),  # full down-projection shape at M = 16
     (16, 11008, 4096, "f16", "f16"),  # full gate/up shape at M = 16
+    (16, 5120, 4096, "f16", "f32"),   # two row tiles per workgroup, four phases
+    (9, 6001, 4096, "f16", "bf16"),   # two row tiles per workgroup, ragged last tile
     (16, 777, 1024, "bf16", "f32"),
     (1, 520, 11008, "f16", "f32"),    # three activation phases at m = 1
     (2, 300, 11008, "f16", "f16"),    # four staged rows, three phases

@@ -634,8 +634,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
 }
 
 // INT4 weights x fp16 activations GEMM (m > 16, prefill).  Workgroup tile
-// 128 (m) x 256 (n), 4 waves side by side along n, each 128 x 64 = 8 x 4
-// MFMA tiles of 16x16; K advances one group (128) per step.  Every code is
+// 128 (m) x 256 (n), NWG waves side by side along n (8: each 128 x 32 =
+// 8 x 2 MFMA tiles of 16x16, two waves per SIMD); K advances one group (128)
+// per step.  Every code is
 // dequantized in registers by the wave that uses it, so the vector work per
 // MFMA falls with the rows a wave covers; 128-row waves keep it under the
 // matrix-core time on gfx950 (a wave64 vector instruction issues in about 4
@@ -685,7 +686,22 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave;                           // the wave's rows: wn * 16 * NF + [0, 16 * NF)
   const int nl = lane & 15, kq = lane >> 4;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // Tile of this workgroup.  Workgroups are dispatched to the 8 XCDs round
+  // robin (workgroup i to XCD i % 8), each XCD with its own L2: tile t
+  // goes to workgroup (t % (T/8)) * 8 + t / (T/8) (T rounded down to a
+  // multiple of 8; the rest keep their index), so every XCD runs a
+  // contiguous run of T/8 tiles.  Tiles are numbered in groups of GM m-tiles
+  // by all n-tiles, so such a run is a block of about GM x (T/8/GM) tiles:
+  // each activation row block and each code column block is fetched from
+  // HBM by few XCDs.
+  constexpr int GM = 4;
+  const int ntn = (a.n + BN - 1) / BN, ntm = (a.m + BM - 1) / BM;
+  const int full = (ntn * ntm) & ~7;
+  const int bid = blockIdx.x;
+  const int tile = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
+  const int grp = tile / (GM * ntn), gm = min(ntm - grp * GM, GM);
+  const int tr = tile - grp * GM * ntn;
+  const int m0 = (grp * GM + tr % gm) * BM, n0 = (tr / gm) * BN;
   const int G = a.G;
   const int SCB = (BN * G * 2 + 1023) / 1024 * 1024;
   const int ZCB = (BN * a.zb + 1023) / 1024 * 1024;
@@ -705,23 +721,25 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
     }
   }
 
-  // per-lane source offsets of the direct loads (a group adds a uniform one)
-  const char* const xb = reinterpret_cast<const char*>(a.x);
-  const char* const cb = reinterpret_cast<const char*>(a.codes);
+  // per-lane source offsets of the direct loads, relative to the tile's
+  // first activation row and first code row (a group adds a uniform one);
+  // 32 bits hold them for k up to 2^23
+  const char* const xb = reinterpret_cast<const char*>(a.x) + (int64_t)m0 * a.k * 2;
+  const char* const cb = reinterpret_cast<const char*>(a.codes) + (int64_t)n0 * (a.k / 2);
   uint32_t xoff[XI], woff[WI];
 #pragma unroll
   for (int t = 0; t < XI; ++t) {
     const int i = t * NW + wave;                 // load i fills slots 64 i .. 64 i + 63
     const int r = i * 4 + (lane >> 4);
     const int c16 = (lane & 15) ^ (r & 15);
-    xoff[t] = (uint32_t)(min(m0 + r, a.m - 1) * a.k * 2 + c16 * 16);
+    xoff[t] = (uint32_t)min(r, a.m - 1 - m0) * (uint32_t)(a.k * 2) + c16 * 16;
   }
 #pragma unroll
   for (int t = 0; t < WI; ++t) {
     const int i = t * NW + wave;
     const int row = i * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);   // chunk c of a row sits at slot c ^ ((row >> 2) & 3)
-    woff[t] = (uint32_t)(min(n0 + row, a.n - 1) * (a.k / 2) + c * 16);
+    woff[t] = (uint32_t)min(row, a.n - 1 - n0) * (uint32_t)(a.k / 2) + c * 16;
   }
   // direct loads of group g (clamped: groups past the end reload the last
   // one, so every step issues the same loads)
@@ -815,10 +833,21 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
 
 template <int YDT>
 hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)((a.m + 127) / 128));
   constexpr int NWG = kGemmWaves;
-  gemm_i4_kernel<YDT, NWG><<<grid, NWG * 64, 0, s>>>(a);
-  return hipGetLastError();
+  // one launch per slice of rows keeps the 1-D grid within 2^22 workgroups
+  const int64_t ntn = (a.n + 255) / 256, ysz = YDT == WQ_F32 ? 4 : 2;
+  const int64_t rows = 128 * std::max<int64_t>(1, (int64_t(1) << 22) / ntn);
+  for (int64_t r0 = 0; r0 < a.m; r0 += rows) {
+    GemmArgs b = a;
+    b.m = (int)std::min<int64_t>(a.m - r0, rows);
+    b.x = a.x + r0 * a.k;
+    b.y = static_cast<char*>(a.y) + r0 * a.n * ysz;
+    const dim3 grid((unsigned)(ntn * ((b.m + 127) / 128)));
+    gemm_i4_kernel<YDT, NWG><<<grid, NWG * 64, 0, s>>>(b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- launch

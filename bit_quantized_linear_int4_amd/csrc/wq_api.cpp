@@ -11,7 +11,10 @@ using namespace wq;
 
 namespace {
 
-constexpr int64_t kMaxElems = int64_t(1) << 38;
+// Size limits: every dimension below 2^23 and every matrix at most 2^34
+// elements, so every launch's grid stays within 32-bit work-item counts.
+constexpr int64_t kMaxDim = int64_t(1) << 23;
+constexpr int64_t kMaxElems = int64_t(1) << 34;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool is16(int32_t dt) { return dt == WQ_F16 || dt == WQ_BF16; }
@@ -21,8 +24,7 @@ uintptr_t dt_bytes(int32_t dt) { return dt == WQ_F32 ? 4 : 2; }
 wq_status hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_HIP; }
 
 bool sizes_ok(int64_t n, int64_t k) {
-  return n >= 1 && k >= 1 && n < (int64_t(1) << 31) && k < (int64_t(1) << 31) &&
-         n <= kMaxElems / k;
+  return n >= 1 && k >= 1 && n < kMaxDim && k < kMaxDim && n <= kMaxElems / k;
 }
 
 // Validates a weight descriptor for the given use.  `linear_w4` restricts to
@@ -127,7 +129,7 @@ wq_status wq_pack_nf4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t 
 }
 
 size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w) {
-  if (m < 1 || m >= (int64_t(1) << 31) || check_weight(w, true) != WQ_OK) return 0;
+  if (m < 1 || m >= kMaxDim || check_weight(w, true) != WQ_OK) return 0;
   return plan_w4a16(m, w).ws;
 }
 
@@ -137,7 +139,7 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight
   const wq_status ws = check_weight(w, true);
   if (ws != WQ_OK) return ws;
   if (!is16(xdt) || !is_out(ydt)) return WQ_ERR_UNSUPPORTED;
-  if (m < 1 || m >= (int64_t(1) << 31) || m > kMaxElems / w->k || m > kMaxElems / w->n)
+  if (m < 1 || m >= kMaxDim || m > kMaxElems / w->k || m > kMaxElems / w->n)
     return WQ_ERR_SHAPE;
   if (w->k % 128 != 0) return WQ_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;

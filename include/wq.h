@@ -30,6 +30,9 @@
  *    error other than WQ_ERR_HIP has enqueued nothing.  WQ_ERR_HIP reports
  *    a failed kernel launch.  NaN/Inf inputs are not checked and give
  *    unspecified (but memory-safe) results.
+ *  - Sizes: every dimension (m, n, k) is below 2^23 and every matrix
+ *    (n x k weights, m x k activations, m x n outputs) holds at most 2^34
+ *    elements; larger sizes return WQ_ERR_SHAPE.
  *  - Rounding: every "round" is round-half-to-even; every division is an
  *    IEEE fp32 division; 16-bit conversions round to nearest even.
  *  - The library's only mutable global state is the per-kernel LDS limit it

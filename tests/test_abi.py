@@ -134,6 +134,12 @@ def test_linear_w4a16_argument_errors():
     assert call(ydt=7) == UNSUP
     assert call(w=_weight(fmt=wq.FMT_INT8_SYM_ROW, group=256)) == UNSUP
     assert call(w=_weight(fmt=wq.FMT_NF4, group=64, zeros=None, scales2=A16, group2=128)) == UNSUP
+    # size limits: every dimension below 2^23, every matrix at most 2^34 elements
+    assert call(m=1 << 23) == SHAPE
+    assert call(w=_weight(n=1 << 23, k=128)) == SHAPE
+    assert call(w=_weight(n=(1 << 21) + 16, k=8192)) == SHAPE     # n * k > 2^34
+    assert call(m=(1 << 21) + 1, w=_weight(n=4096, k=8192)) == SHAPE   # m * k > 2^34
+    assert _lib().wq_linear_w4a16_workspace(1 << 23, ctypes.byref(_weight())) == 0
     # no decode or GEMM schedule needs scratch: NULL workspace is accepted
     big = _weight(n=4096, k=16384)
     assert _lib().wq_linear_w4a16_workspace(16, ctypes.byref(big)) == 0

@@ -367,8 +367,15 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     // phase issued so far (each phase issues its code loads, then its
     // activation loads)
     const int later = min(p + NBUF - 1, issued_max) - p;
+    if (SZL && p == 0) {
+      // the staged scale/zero loads precede every phase's loads: once no
+      // more than the NBUF phases' loads are outstanding they have landed,
+      // and the barrier publishes every wave's share without waiting for
+      // any other wave's codes
+      vm_wait<NBUF * (XI + WU)>();
+      wg_barrier();
+    }
     vm_wait_n(later * (XI + WU));
-    if (SZL && p == 0) wg_barrier();   // every wave's staged scale/zero loads have landed
     asm volatile("" ::: "memory");
     const uint4_t* buf = ring + b * XS + mrow * (16 * GPP);
 #pragma unroll

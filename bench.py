@@ -82,55 +82,81 @@ def _int4_weight(wq, torch, w_np):
 
 
 class W4Layers(Workload):
-    """INT4 layers, each applied to its own seeded input (decode or prefill)."""
+    """INT4 layers, each applied to its own seeded input (decode or prefill).
+    A gate projection followed by an up projection of the same input runs
+    as one pair call (the activations are read once for both)."""
 
     def setup(self):
         import torch
         import bit_quantized_linear_int4_amd as wq
         self.wq = wq
         base, self.xs, self.ys = [], [], []
-        self.bytes, self.flops = [], []
+        bytes_, flops = [], []
         for _, x, w in self.layers_np:
             qw = _int4_weight(wq, torch, w)
             base.append(qw)
             m, n, k = x.shape[0], w.shape[0], w.shape[1]
             self.xs.append(torch.from_numpy(x).cuda())
             self.ys.append(torch.empty((m, n), dtype=torch.float16, device="cuda"))
-            self.bytes.append(qw.nbytes() + x.size * 2 + m * n * 2)
-            self.flops.append(2 * m * n * k)
+            bytes_.append(qw.nbytes() + x.size * 2 + m * n * 2)
+            flops.append(2 * m * n * k)
             assert wq.wq_linear_w4a16_workspace(m, qw) == 0
         torch.cuda.synchronize()
         reps = _copies_needed(sum(q.nbytes() for q in base))
         self.copies = [base] + [[q.clone() for q in base] for _ in range(reps - 1)]
         torch.cuda.synchronize()
-        # dominant kernel: the layer shape that takes most of the step
-        # (gate/up share one kernel configuration in the decode step)
-        shapes = [(x.shape[0], w.shape[0], w.shape[1]) for _, x, w in self.layers_np]
+        # call units: (i,) one layer; (i, j) a gate/up pair sharing x
+        names = [nm for nm, _, _ in self.layers_np]
+        self.units, i = [], 0
+        while i < len(names):
+            if (i + 1 < len(names) and names[i] == "gate" and names[i + 1] == "up"
+                    and self.layers_np[i][1] is self.layers_np[i + 1][1]):
+                self.units.append((i, i + 1))
+                i += 2
+            else:
+                self.units.append((i,))
+                i += 1
+        # algorithmic work of a unit (a pair reads x once)
+        self.ubytes = [sum(bytes_[j] for j in u) - (len(u) - 1) * self.layers_np[u[0]][1].size * 2
+                       for u in self.units]
+        self.uflops = [sum(flops[j] for j in u) for u in self.units]
+        # dominant kernel: the unit shape whose launches take most of the step
         groups = {}
-        for i, s in enumerate(shapes):
-            groups.setdefault(s, []).append(i)
-        self.dom = max(groups.values(), key=lambda idx: (len(idx), -idx[0]))
-        m, n, k = shapes[self.dom[0]]
+        for ui, u in enumerate(self.units):
+            key = tuple((self.layers_np[j][1].shape[0],) + self.layers_np[j][2].shape for j in u)
+            groups.setdefault(key, []).append(ui)
+        per = self.ubytes if self.unit == "GB/s" else self.uflops
+        self.dom = max(groups.values(), key=lambda idx: (sum(per[ui] for ui in idx), -idx[0]))
+        u0 = self.units[self.dom[0]]
+        m, n, k = self.layers_np[u0[0]][1].shape[0], *self.layers_np[u0[0]][2].shape
         fam = "stream dequant-GEMV" if m <= 16 else "dequant-GEMM"
         self.kernel = "stream" if m <= 16 else "gemm"
-        names = "/".join(self.layers_np[i][0] for i in self.dom)
-        self.kernel_desc = f"w4a16 {fam} ({names}: M={m}, N={n}, K={k})"
+        names_dom = "/".join("+".join(self.layers_np[j][0] for j in self.units[ui])
+                             for ui in self.dom)
+        pair = " pair" if len(u0) == 2 else ""
+        self.kernel_desc = f"w4a16 {fam}{pair} ({names_dom}: M={m}, N={n}, K={k})"
 
-    def _call(self, copy, i):
+    def _call(self, copy, ui):
         wq, ws = self.wq, self.copies[copy % len(self.copies)]
+        u = self.units[ui]
+        if len(u) == 2:
+            i, j = u
+            return lambda: wq.wq_linear_w4a16_gate_up(self.xs[i], ws[i], ws[j], self.ys[i],
+                                                      self.ys[j], act=0)
+        i = u[0]
         return lambda: wq.wq_linear_w4a16(self.xs[i], ws[i], self.ys[i], None)
 
     def step_calls(self, copy):
-        return [self._call(copy, i) for i in range(len(self.layers_np))]
+        return [self._call(copy, ui) for ui in range(len(self.units))]
 
     def dominant_calls(self, copy):
-        return [self._call(copy, i) for i in self.dom]
+        return [self._call(copy, ui) for ui in self.dom]
 
     def work_per_step(self):
-        return sum(self.bytes) if self.unit == "GB/s" else sum(self.flops)
+        return sum(self.ubytes) if self.unit == "GB/s" else sum(self.uflops)
 
     def dominant_work(self):
-        per = self.bytes if self.unit == "GB/s" else self.flops
+        per = self.ubytes if self.unit == "GB/s" else self.uflops
         return per[self.dom[0]]
 
     def cpu_sample(self):
@@ -162,6 +188,7 @@ class W4Layers(Workload):
                 "layers": [{"name": nm, "m": int(x.shape[0]), "n": int(w.shape[0]),
                             "k": int(w.shape[1])} for nm, x, w in self.layers_np],
                 "format": "INT4 asymmetric, group 128, fp16 scale, 4-bit zero",
+                "calls": ["+".join(self.layers_np[j][0] for j in u) for u in self.units],
                 "weight_copies": len(self.copies)}
 
 

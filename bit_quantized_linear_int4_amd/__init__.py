@@ -18,7 +18,7 @@ __all__ = [
     "WqError", "QuantizedWeight", "F16", "BF16", "F32",
     "FMT_INT4_ASYM", "FMT_NF4", "FMT_INT8_SYM_ROW",
     "wq_quantize_groupwise", "wq_pack_nf4", "wq_nf4_codebook",
-    "wq_linear_w4a16_workspace", "wq_linear_w4a16",
+    "wq_linear_w4a16_workspace", "wq_linear_w4a16", "wq_linear_w4a16_gate_up",
     "wq_int8_prepare_activations", "wq_linear_int8_decomp_workspace",
     "wq_linear_int8_decomp", "wq_dequantize", "wq_status_string",
     "alloc_int4", "alloc_nf4", "alloc_int8", "library_path",
@@ -73,6 +73,8 @@ def _load():
         "wq_linear_w4a16_workspace": (ctypes.c_size_t, [c_i64, wp]),
         "wq_linear_w4a16": (c_i32, [c_vp, c_i32, c_i64, wp, c_vp, c_i32, c_vp,
                                     ctypes.c_size_t, c_vp]),
+        "wq_linear_w4a16_gate_up": (c_i32, [c_vp, c_i32, c_i64, wp, wp, c_i32, c_vp, c_vp,
+                                            c_i32, c_vp]),
         "wq_int8_prepare_activations": (c_i32, [c_vp, c_i64, c_i64, c_f, c_vp, c_vp, c_vp,
                                                 c_vp, c_vp, c_vp]),
         "wq_linear_int8_decomp_workspace": (ctypes.c_size_t, [c_i64, c_i64]),
@@ -209,6 +211,14 @@ def wq_linear_w4a16(x, weight, y, workspace=None, stream=None):
     st = _load().wq_linear_w4a16(_ptr(x), _dt(x), x.shape[0], ctypes.byref(d), _ptr(y), _dt(y),
                                  _ptr(workspace), ws_bytes, _stream(stream, x))
     _check(st, "wq_linear_w4a16")
+
+
+def wq_linear_w4a16_gate_up(x, w_gate, w_up, y_gate, y_up=None, act=0, stream=None):
+    dg, du = w_gate.descriptor(), w_up.descriptor()
+    st = _load().wq_linear_w4a16_gate_up(_ptr(x), _dt(x), x.shape[0], ctypes.byref(dg),
+                                         ctypes.byref(du), int(act), _ptr(y_gate), _ptr(y_up),
+                                         _dt(y_gate), _stream(stream, x))
+    _check(st, "wq_linear_w4a16_gate_up")
 
 
 def wq_int8_prepare_activations(x, threshold, mask, idx, count, qx, sx, stream=None):

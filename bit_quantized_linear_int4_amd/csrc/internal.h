@@ -74,6 +74,11 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w);
 hipError_t launch_w4a16(const void* x, int xdt, int64_t m, const wq_weight* w,
                         const float* levels16, void* y, int ydt, void* ws,
                         const W4Plan& plan, hipStream_t s);
+// gate/up pair sharing x (INT4, same n and k); act 1: yg = silu(gate) * up
+W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu);
+hipError_t launch_w4a16_pair(const void* x, int xdt, int64_t m, const wq_weight* wg,
+                             const wq_weight* wu, int act, void* yg, void* yu, int ydt,
+                             const W4Plan& plan, hipStream_t s);
 
 hipError_t launch_int8_prepare(const uint16_t* x, int64_t m, int64_t k, float thr,
                                uint8_t* mask, int32_t* idx, int32_t* count, int8_t* qx,

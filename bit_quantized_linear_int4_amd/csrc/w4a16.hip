@@ -99,6 +99,13 @@ struct SkinnyArgs {
   int m, n, k, G, zb;        // zb = bytes per row of zeros
   float* partial;            // [splits][m][n] when the K range is split
   void* y;
+  // second INT4 matrix of a gate/up pair (same n, k; same x), its output,
+  // and the epilogue: 0 = both outputs, 1 = y = silu(gate) * up only
+  const uint32_t* codes_b;
+  const void* scales_b;
+  const uint8_t* zeros_b;
+  void* y_b;
+  int act;
 };
 
 struct Levels {
@@ -232,9 +239,17 @@ __device__ __forceinline__ void vm_wait_n(int n) { vm_wait_range<0, 63>(n); }
 // The 16-byte chunk c16 of activation row m sits in slot c16 ^ (m & 15) of
 // the row, so the 16 rows an MFMA operand read touches fall in different LDS
 // banks.  LDS is sized at launch (stream_lds_bytes).
-template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL>
+template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL,
+          bool DUAL>
 __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv, int phases,
                                                          int kslice) {
+  // DUAL: TPG counts the tiles of both matrices; tile t < TH is row tile t
+  // of the first (gate) matrix, tile TH + t the same rows of the second (up)
+  constexpr int TH = DUAL ? TPG / 2 : TPG;                 // row tiles per workgroup
+  static_assert(!DUAL || (TPG % 2 == 0 && FMT == WQ_FMT_INT4_ASYM), "pairs are INT4");
+  // codes through a per-wave LDS ring (staged scales, one matrix); else in
+  // registers
+  constexpr bool CRING = SZL && !DUAL;
   constexpr int CG = NW * GPP;                             // groups per phase
   constexpr int XS = (MP * GPP * 16 + 63) / 64 * 64;       // slots per wave buffer
   constexpr int XI = XS / 64;                              // direct loads per phase
@@ -257,10 +272,15 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   const int ZCB = (16 * a.zb + 1023) / 1024 * 1024;
   uint8_t* const scl = reinterpret_cast<uint8_t*>(dsm + NW * NBUF * XS);
   uint8_t* const zcl = scl + TPG * SCB;
-  // SZL: the codes also arrive through LDS (per-wave ring, 1 KB per unit:
+  // CRING: the codes also arrive through LDS (per-wave ring, 1 KB per unit:
   // lane l's 16 bytes at slot l), so no load inside the loop lands in a
   // register and the compiler adds no waits of its own
   uint4_t* const wring = reinterpret_cast<uint4_t*>(zcl + TPG * ZCB) + wave * NBUF * TPG * GPP * 64;
+  // row tile and matrix of tile t
+  auto tile_of = [&](int t) {
+    return min((int)blockIdx.x + (t % TH) * (int)gridDim.x, ntiles - 1);
+  };
+  auto second = [&](int t) { return DUAL && t >= TH; };
 
   if constexpr (FMT == WQ_FMT_NF4) {
     if (tid < 16) lut[tid] = lv.v[tid];
@@ -271,15 +291,16 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     // waves; chunks past the end of a buffer reload its last 16 bytes
     const int nsc = SCB / 1024, nzc = ZCB / 1024, per = nsc + nzc;
     const int64_t sbytes = (int64_t)a.n * a.G * 2, zbytes = (int64_t)a.n * a.zb;
-    const uint8_t* sbase = static_cast<const uint8_t*>(a.scales);
     for (int i = wave; i < TPG * per; i += NW) {
       const int t = i / per, j = i % per;
-      const int tile = min((int)blockIdx.x + t * (int)gridDim.x, ntiles - 1);
+      const int tile = tile_of(t);
       const bool isz = j >= nsc;
       const int jj = isz ? j - nsc : j;
       const int64_t off = (int64_t)tile * 16 * (isz ? a.zb : 2 * a.G) + jj * 1024 + lane * 16;
       const int64_t lim = (isz ? zbytes : sbytes) - 16;
-      const uint8_t* src = (isz ? a.zeros : sbase) + min(off, lim);
+      const uint8_t* zsrc = second(t) ? a.zeros_b : a.zeros;
+      const uint8_t* ssrc = static_cast<const uint8_t*>(second(t) ? a.scales_b : a.scales);
+      const uint8_t* src = (isz ? zsrc : ssrc) + min(off, lim);
       uint8_t* dst = (isz ? zcl + t * ZCB : scl + t * SCB) + jj * 1024;
       lds_dma16(src, (lds_void_t*)dst);
     }
@@ -304,7 +325,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     }
   };
 
-  const uint4_t* q4 = reinterpret_cast<const uint4_t*>(a.codes);
+  const uint4_t* q4a = reinterpret_cast<const uint4_t*>(a.codes);
+  const uint4_t* q4b = reinterpret_cast<const uint4_t*>(DUAL ? a.codes_b : a.codes);
   const int k32 = a.k / 32;
   const bool dq = a.scales2 != nullptr;
   const float* s2p = dq ? a.scales2 : static_cast<const float*>(a.scales);
@@ -317,12 +339,12 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     constexpr int b = decltype(bc)::value;
 #pragma unroll
     for (int t = 0; t < TPG; ++t) {
-      const int tile = min((int)blockIdx.x + t * (int)gridDim.x, ntiles - 1);
-      const int row = min(tile * 16 + nl, a.n - 1);
+      const int row = min(tile_of(t) * 16 + nl, a.n - 1);
+      const uint4_t* q4 = second(t) ? q4b : q4a;
 #pragma unroll
       for (int u = 0; u < GPP; ++u) {
         const int g = min(gbeg + p * CG + wave * GPP + u, a.G - 1);
-        if constexpr (SZL) {
+        if constexpr (CRING) {
           lds_dma16(q4 + (int64_t)row * k32 + g * 4 + kq,
                     (lds_void_t*)(wring + ((b * TPG + t) * GPP + u) * 64));
         } else {
@@ -330,8 +352,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
         }
         if constexpr (SZL) {
         } else if constexpr (FMT == WQ_FMT_INT4_ASYM) {
-          sv[b][t][u] = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)row * a.G + g]);
-          zv[b][t][u] = a.zeros[(int64_t)row * a.zb + (g >> 1)];
+          const uint16_t* sp = static_cast<const uint16_t*>(second(t) ? a.scales_b : a.scales);
+          sv[b][t][u] = f16_bits_to_f32(sp[(int64_t)row * a.G + g]);
+          zv[b][t][u] = (second(t) ? a.zeros_b : a.zeros)[(int64_t)row * a.zb + (g >> 1)];
         } else {
           // the first-level absmax (int8 code or fp32) and the second-level
           // scale (a harmless reload of element 0 without double quantization)
@@ -346,10 +369,25 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     }
   };
 
+  // the loads of one phase.  With codes in registers the activation loads
+  // go first: the compiler's own wait before the first use of a phase's
+  // code registers counts only register loads, so the loads it forces to
+  // complete beyond the explicit wait are the next phase's activation
+  // loads (L2 hits), not its code loads.
+  auto issue_phase = [&](int p, auto bc) {
+    if constexpr (CRING) {
+      issue_w(p, bc);
+      issue_x(p);
+    } else {
+      issue_x(p);
+      issue_w(p, bc);
+    }
+  };
+
   // prologue: phases 0 .. NBUF-1 (always issued; phases past the end load
   // clamped addresses, which keeps the load count fixed)
   [&]<int... B>(std::integer_sequence<int, B...>) {
-    ((issue_w(B, std::integral_constant<int, B>{}), issue_x(B)), ...);
+    (issue_phase(B, std::integral_constant<int, B>{}), ...);
   }(std::make_integer_sequence<int, NBUF>{});
   asm volatile("" ::: "memory");
 
@@ -363,9 +401,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
 
   auto step = [&](int p, auto bc) {
     constexpr int b = decltype(bc)::value;
-    // loads issued after this phase's activation loads: those of every later
-    // phase issued so far (each phase issues its code loads, then its
-    // activation loads)
+    // loads issued after this phase's: those of every later phase issued so
+    // far
     const int later = min(p + NBUF - 1, issued_max) - p;
     if (SZL && p == 0) {
       // the staged scale/zero loads precede every phase's loads: once no
@@ -385,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
         if constexpr (SZL) {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
-            wv[b][t][u] = wring[((b * TPG + t) * GPP + u) * 64 + lane];
+            if constexpr (CRING) wv[b][t][u] = wring[((b * TPG + t) * GPP + u) * 64 + lane];
             const uint16_t sc = *reinterpret_cast<const uint16_t*>(scl + t * SCB + (nl * a.G + g) * 2);
             sv[b][t][u] = f16_bits_to_f32(sc);
             zv[b][t][u] = zcl[t * ZCB + nl * a.zb + (g >> 1)];
@@ -433,8 +470,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     // complete: their values fed the MFMAs above)
     if (p + NBUF < phases) {
       asm volatile("" ::: "memory");
-      issue_w(p + NBUF, bc);
-      issue_x(p + NBUF);
+      issue_phase(p + NBUF, bc);
       asm volatile("" ::: "memory");
     }
   };
@@ -454,7 +490,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     for (int e = 0; e < 4; ++e) red[((wave * TPG + t) * 4 + e) * kWave + lane] = acc[t][e];
   __syncthreads();
   constexpr int NV = TPG * 4 * kWave;
-  for (int i = tid; i < NV; i += NW * 64) {
+  constexpr int NH = TH * 4 * kWave;                 // the second matrix's sums start here
+  for (int i = tid; i < NH; i += NW * 64) {
     const int te = i / kWave, l = i % kWave, t = te / 4, e = te % 4;
     const int mm = (l >> 4) * 4 + e;
     const int tile = (int)blockIdx.x + t * (int)gridDim.x;
@@ -463,6 +500,19 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       float v = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += red[i + w * NV];
+      if constexpr (DUAL) {
+        float v2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v2 += red[i + NH + w * NV];
+        const int64_t o = (int64_t)mm * a.n + nn;
+        if (a.act) {
+          store_y<YDT>(a.y, o, v / (1.0f + expf(-v)) * v2);   // silu(gate) * up
+        } else {
+          store_y<YDT>(a.y, o, v);
+          store_y<YDT>(a.y_b, o, v2);
+        }
+        continue;
+      }
       if (gridDim.y > 1)
         a.partial[((int64_t)blockIdx.y * a.m + mm) * a.n + nn] = v;
       else
@@ -483,12 +533,13 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
 }
 
 // Dynamic LDS bytes of one stream_kernel workgroup.
-inline size_t stream_lds_bytes(int nw, int tpg, int gpp, int mp, int nbuf, bool szl, int G, int zb) {
+inline size_t stream_lds_bytes(int nw, int tpg, int gpp, int mp, int nbuf, bool szl, bool dual,
+                               int G, int zb) {
   const size_t xs = (size_t)((mp * gpp * 16 + 63) / 64 * 64) * 16;
   size_t b = (size_t)nw * nbuf * xs;
   if (szl)
     b += (size_t)tpg * ((32 * G + 1023) / 1024 * 1024 + (16 * zb + 1023) / 1024 * 1024) +
-         (size_t)nw * nbuf * tpg * gpp * 1024;
+         (dual ? 0 : (size_t)nw * nbuf * tpg * gpp * 1024);
   const size_t red = (size_t)nw * tpg * 4 * 64 * 4;
   return b > red ? b : red;
 }
@@ -859,10 +910,11 @@ hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------- launch
 // Streaming decode configurations: NW, TPG, GPP, MP, NBUF.
-template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL>
+template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL,
+          bool DUAL = false>
 hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
-  auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL>;
-  const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, a.G, a.zb);
+  auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL, DUAL>;
+  const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, DUAL, a.G, a.zb);
   if (a.m > MP) return hipErrorInvalidValue;   // rows past MP are never staged
   if (lds > 160 * 1024 - 256) return hipErrorInvalidConfiguration;
   // raise the dynamic LDS limit of this instantiation when a launch needs
@@ -906,10 +958,34 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
     WQ_STR(46, 8, 1, 1, 16, 3)
     WQ_STR(47, 8, 1, 2, 1, 2)
     WQ_STR(50, 8, 2, 1, 16, 2)
+    WQ_STR(51, 8, 4, 1, 16, 2)
     WQ_STR(54, 8, 2, 1, 4, 2)
     default: return hipErrorInvalidConfiguration;
   }
 #undef WQ_STR
+}
+
+// Gate/up pair configurations: NW, TPG (tiles of both matrices), GPP, MP, NBUF.
+template <int XDT, int YDT>
+hipError_t launch_stream_pair(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
+                              hipStream_t s) {
+#define WQ_PAIR(C, NW, TPG, GPP, MP, NBUF)                                                    \
+  case C:                                                                                     \
+    if (p.szl)                                                                                \
+      return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, true, true>( \
+          a, lv, p, s);                                                                       \
+    return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, false, true>(  \
+        a, lv, p, s);
+  switch (p.cfg) {
+    WQ_PAIR(60, 8, 2, 1, 1, 2)
+    WQ_PAIR(61, 8, 2, 1, 4, 2)
+    WQ_PAIR(62, 8, 2, 1, 16, 2)
+    WQ_PAIR(63, 8, 4, 1, 16, 2)
+    WQ_PAIR(64, 8, 6, 1, 16, 2)
+    WQ_PAIR(65, 8, 8, 1, 16, 2)
+    default: return hipErrorInvalidConfiguration;
+  }
+#undef WQ_PAIR
 }
 
 template <int XDT, int YDT>
@@ -956,6 +1032,29 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
                               : launch_stream<XDT, YDT, WQ_FMT_INT4_ASYM>(a, lv, p, s);
 }
 
+template <int XDT, int YDT>
+hipError_t launch_pair_typed(const void* x, int64_t m, const wq_weight* wg, const wq_weight* wu,
+                             int act, void* yg, void* yu, const W4Plan& p, hipStream_t s) {
+  Levels lv{};
+  SkinnyArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.codes = static_cast<const uint32_t*>(wg->codes);
+  a.scales = wg->scales;
+  a.zeros = wg->zeros;
+  a.m = (int)m;
+  a.n = (int)wg->n;
+  a.k = (int)wg->k;
+  a.G = (int)(wg->k / 128);
+  a.zb = (a.G + 1) / 2;
+  a.y = yg;
+  a.codes_b = static_cast<const uint32_t*>(wu->codes);
+  a.scales_b = wu->scales;
+  a.zeros_b = wu->zeros;
+  a.y_b = yu;
+  a.act = act;
+  return launch_stream_pair<XDT, YDT>(a, lv, p, s);
+}
+
 template <int XDT>
 hipError_t launch_x(const void* x, int64_t m, const wq_weight* w, const float* levels, void* y,
                     int ydt, void* ws, const W4Plan& p, hipStream_t s) {
@@ -975,7 +1074,8 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   static const SCfg scfgs[] = {
       {22, 8, 1, 1, 1, 4},  {27, 8, 3, 1, 16, 4},  {40, 8, 1, 1, 1, 2},  {41, 8, 1, 1, 1, 3},
       {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2},  {44, 8, 3, 1, 16, 3},  {45, 8, 1, 1, 16, 2},
-      {46, 8, 1, 1, 16, 3},  {47, 8, 1, 2, 1, 2},  {50, 8, 2, 1, 16, 2},  {54, 8, 2, 1, 4, 2}};
+      {46, 8, 1, 1, 16, 3},  {47, 8, 1, 2, 1, 2},  {50, 8, 2, 1, 16, 2},  {51, 8, 4, 1, 16, 2},
+      {54, 8, 2, 1, 4, 2}};
   W4Plan p;
   p.path = m > 16 ? 1 : 3;
   p.tpg = 1;
@@ -1001,7 +1101,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   //  m = 1: eight waves, one group per wave and phase (two for long K);
   //  m <= 4: eight waves, one tile;
   //  m <= 16: one workgroup per CU, as many tiles per workgroup as that
-  //           takes (at most 3).
+  //           takes (at most 4; more tiles take several rounds).
   int cfg;
   if (m <= 1) {
     cfg = G >= 64 ? 47 : 40;
@@ -1009,7 +1109,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
     cfg = 42;
   } else {
     const int64_t tpg = (ntiles + 255) / 256;
-    cfg = tpg >= 3 ? 43 : (tpg == 2 ? 50 : 45);
+    cfg = tpg >= 4 ? 51 : tpg == 3 ? 43 : (tpg == 2 ? 50 : 45);
   }
   int splits = 1;
 #ifdef WQ_TUNE_ENV
@@ -1038,8 +1138,8 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
       if (p.splits > 1) p.ws = (size_t)p.splits * (size_t)m * (size_t)w->n * sizeof(float);
       // staged scales must fit beside the activation ring
       if (p.szl) {
-        const size_t lds = stream_lds_bytes(sc.nw, sc.tpg, sc.gpp, sc.mp, sc.nbuf, true, (int)G,
-                                            (int)((G + 1) / 2));
+        const size_t lds = stream_lds_bytes(sc.nw, sc.tpg, sc.gpp, sc.mp, sc.nbuf, true, false,
+                                            (int)G, (int)((G + 1) / 2));
         if (lds > 160 * 1024 - 256) p.szl = false;
       }
     }
@@ -1051,6 +1151,70 @@ hipError_t launch_w4a16(const void* x, int xdt, int64_t m, const wq_weight* w,
                         hipStream_t s) {
   if (xdt == WQ_BF16) return launch_x<WQ_BF16>(x, m, w, levels16, y, ydt, ws, plan, s);
   return launch_x<WQ_F16>(x, m, w, levels16, y, ydt, ws, plan, s);
+}
+
+W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
+  // Gate/up pairs (m <= 16): the single-matrix schedules with the tiles of
+  // both matrices in one workgroup (codes in registers, scales staged), so
+  // the activations are staged once for both.
+  struct PCfg { int id, nw, tpg, gpp, mp, nbuf; };
+  static const PCfg pcfgs[] = {{60, 8, 2, 1, 1, 2},  {61, 8, 2, 1, 4, 2}, {62, 8, 2, 1, 16, 2},
+                               {63, 8, 4, 1, 16, 2}, {64, 8, 6, 1, 16, 2},
+                               {65, 8, 8, 1, 16, 2}};
+  W4Plan p = plan_w4a16(m, wg);
+  p.szl = p.szl && plan_w4a16(m, wu).szl;
+  if (p.path == 1) return p;
+  const int64_t G = wg->k / 128;
+  const int64_t ntiles = (wg->n + 15) / 16;
+  int cfg;
+  if (m <= 1) {
+    cfg = 60;
+  } else if (m <= 4) {
+    cfg = 61;
+  } else {
+    const int64_t th = (ntiles + 255) / 256;
+    cfg = th >= 4 ? 65 : th == 3 ? 64 : (th == 2 ? 63 : 62);
+  }
+  for (const PCfg& pc : pcfgs)
+    if (pc.id == cfg) {
+      p.cfg = pc.id;
+      p.tpg = pc.tpg;
+      p.gpw = pc.gpp;
+      p.mp = pc.mp;
+      p.splits = 1;
+      p.kslice = (int)G;
+      p.phases = (int)((G + pc.nw * pc.gpp - 1) / (pc.nw * pc.gpp));
+      p.grid = (int)((ntiles + pc.tpg / 2 - 1) / (pc.tpg / 2));
+      p.ws = 0;
+      if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true, (int)G,
+                                    (int)((G + 1) / 2)) > 160 * 1024 - 256)
+        p.szl = false;
+    }
+  return p;
+}
+
+hipError_t launch_w4a16_pair(const void* x, int xdt, int64_t m, const wq_weight* wg,
+                             const wq_weight* wu, int act, void* yg, void* yu, int ydt,
+                             const W4Plan& plan, hipStream_t s) {
+  if (plan.path == 1) {
+    // prefill: two GEMMs (the pair gains nothing once the weights are reused
+    // across many rows)
+    const float* lv = nf4_levels();
+    hipError_t e = launch_w4a16(x, xdt, m, wg, lv, yg, ydt, nullptr, plan, s);
+    if (e != hipSuccess) return e;
+    return launch_w4a16(x, xdt, m, wu, lv, yu, ydt, nullptr, plan_w4a16(m, wu), s);
+  }
+#define WQ_PAIR_Y(XDT)                                                                      \
+  switch (ydt) {                                                                            \
+    case WQ_F32: return launch_pair_typed<XDT, WQ_F32>(x, m, wg, wu, act, yg, yu, plan, s);   \
+    case WQ_BF16: return launch_pair_typed<XDT, WQ_BF16>(x, m, wg, wu, act, yg, yu, plan, s); \
+    default: return launch_pair_typed<XDT, WQ_F16>(x, m, wg, wu, act, yg, yu, plan, s);       \
+  }
+  if (xdt == WQ_BF16) {
+    WQ_PAIR_Y(WQ_BF16)
+  }
+  WQ_PAIR_Y(WQ_F16)
+#undef WQ_PAIR_Y
 }
 
 }  // namespace wq

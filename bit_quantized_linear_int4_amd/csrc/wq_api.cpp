@@ -152,6 +152,31 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight
                                  static_cast<hipStream_t>(stream)));
 }
 
+wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
+                                  const wq_weight* w_gate, const wq_weight* w_up, int32_t act,
+                                  void* y_gate, void* y_up, int32_t ydt, void* stream) {
+  if (x == nullptr || y_gate == nullptr) return WQ_ERR_NULL;
+  if (act != 0 && act != 1) return WQ_ERR_UNSUPPORTED;
+  if (act == 0 && y_up == nullptr) return WQ_ERR_NULL;
+  wq_status st = check_weight(w_gate, true);
+  if (st != WQ_OK) return st;
+  st = check_weight(w_up, true);
+  if (st != WQ_OK) return st;
+  if (w_gate->fmt != WQ_FMT_INT4_ASYM || w_up->fmt != WQ_FMT_INT4_ASYM) return WQ_ERR_UNSUPPORTED;
+  if (!is16(xdt) || !is_out(ydt)) return WQ_ERR_UNSUPPORTED;
+  if (w_gate->n != w_up->n || w_gate->k != w_up->k || w_gate->k % 128 != 0) return WQ_ERR_SHAPE;
+  if (m < 1 || m >= kMaxDim || m > kMaxElems / w_gate->k || m > kMaxElems / w_gate->n)
+    return WQ_ERR_SHAPE;
+  if (act == 1 && m > 16) return WQ_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(y_gate, dt_bytes(ydt)) ||
+      (act == 0 && !aligned(y_up, dt_bytes(ydt))))
+    return WQ_ERR_ALIGN;
+  const W4Plan plan = plan_w4a16_pair(m, w_gate, w_up);
+  return hip_status(launch_w4a16_pair(x, xdt, m, w_gate, w_up, act, y_gate,
+                                      act == 0 ? y_up : nullptr, ydt, plan,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 size_t wq_linear_int8_decomp_workspace(int64_t m, int64_t k) {
   if (m < 1 || k < 16 || k % 16 != 0 || !sizes_ok(m, k)) return 0;
   // mask u8[k] | idx i32[k] | count i32 | qx i8[m][k] | sx f32[m], each 256-aligned

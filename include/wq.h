@@ -190,6 +190,29 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m,
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * The gate and up projections of a gated MLP block ([P3] step 4 lists the
+ * gate, up and down projections of each block) as one call sharing x:
+ *
+ *   act = 0:  y_gate = x * W_gate_hat^T,  y_up = x * W_up_hat^T
+ *             (each exactly what wq_linear_w4a16 computes for it);
+ *   act = 1:  y_gate = silu(g) * u with g, u those two products in fp32
+ *             and silu(v) = v / (1 + exp(-v)); y_up is not written.
+ *
+ * For m <= 16 one pass streams both matrices with the activations staged
+ * once; larger m runs the two GEMMs (act = 1 is decode only).
+ *
+ * x: xdt in {WQ_F16, WQ_BF16}, [m][k], 16-byte aligned.  w_gate, w_up:
+ * INT4_ASYM group 128 with equal n and k.  y_gate, y_up: ydt in
+ * {F16, BF16, F32}, [m][n] each (y_up may be NULL when act = 1).
+ * Errors: WQ_ERR_SHAPE when n or k differ; WQ_ERR_UNSUPPORTED for NF4,
+ * act outside {0, 1}, or act = 1 with m > 16.  No workspace.
+ */
+wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
+                                  const wq_weight* w_gate, const wq_weight* w_up,
+                                  int32_t act, void* y_gate, void* y_up, int32_t ydt,
+                                  void* stream);
+
+/*
  * LLM.int8() activation side ([P1] 2.1; threshold 6.0 in [P5] 6.1):
  *   outlier columns O = { c : |x[i][c]| > threshold for some row i }
  *     (strict); mask[c] = 1 for c in O else 0; idx = ascending list of O,

@@ -34,6 +34,19 @@ def naive(x, w_hat):
     return y
 
 
+def silu_gated(g, u):
+    """silu(g) * u in fp64, silu(v) = v / (1 + exp(-v)): the activation
+    product that joins the gate and up projections of a gated MLP block.
+    The pages list the gate, up and down projections of each block ([P3]
+    step 4) but name no activation; SiLU, the activation of the
+    LLaMA/Qwen2-style blocks those projections belong to, is the reading
+    taken here."""
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
 def max_rel_err(y, y_ref):
     """max|y - y_ref| / max|y_ref| (the float acceptance measure)."""
     y = np.asarray(y, np.float64)

@@ -114,6 +114,30 @@ def _weight(fmt=wq.FMT_INT4_ASYM, n=64, k=256, group=128, codes=A16, scales=A16,
     return d
 
 
+def test_gate_up_argument_errors():
+    f = _lib().wq_linear_w4a16_gate_up
+
+    def call(x=A16, xdt=wq.F16, m=1, wg=None, wu=None, act=0, yg=A16, yu=A16, ydt=wq.F32):
+        wg = _weight() if wg is None else wg
+        wu = _weight() if wu is None else wu
+        return f(x, xdt, m, ctypes.byref(wg), ctypes.byref(wu), act, yg, yu, ydt, None)
+
+    assert call(x=None) == NULL
+    assert call(yg=None) == NULL
+    assert call(yu=None) == NULL                      # act 0 writes both outputs
+    assert call(wu=_weight(zeros=None)) == NULL
+    assert call(act=2) == UNSUP
+    assert call(act=1, m=17) == UNSUP                 # the SiLU product is decode only
+    assert call(wu=_weight(n=128)) == SHAPE           # the pair shares n and k
+    assert call(wu=_weight(k=384)) == SHAPE
+    assert call(m=0) == SHAPE
+    assert call(m=1 << 23) == SHAPE
+    assert call(wg=_weight(fmt=wq.FMT_NF4, group=64, zeros=None)) == UNSUP
+    assert call(xdt=wq.F32) == UNSUP
+    assert call(x=ODD) == ALIGN
+    assert call(yu=ODD, act=0) == ALIGN
+
+
 def test_linear_w4a16_argument_errors():
     f = _lib().wq_linear_w4a16
 

@@ -120,6 +120,7 @@ def oracle_linear(x_np, w_np, xdt, rows=None):
     (16, 11008, 4096, "f16", "f16"),  # full gate/up shape at M = 16
     (16, 5120, 4096, "f16", "f32"),   # two row tiles per workgroup, four phases
     (9, 6001, 4096, "f16", "bf16"),   # two row tiles per workgroup, ragged last tile
+    (16, 14336, 4096, "f16", "f32"),  # four row tiles per workgroup (8B MLP width)
     (16, 777, 1024, "bf16", "f32"),
     (1, 520, 11008, "f16", "f32"),    # three activation phases at m = 1
     (2, 300, 11008, "f16", "f16"),    # four staged rows, three phases
@@ -152,6 +153,65 @@ def test_linear_gemm_parity(m, n, k, xdt, ydt):
     w = workloads.weights(n, k, seed, 1, dtype=xdt)
     y, _ = run_linear(x, w, xdt, ydt)
     rel = check_close(y, oracle_linear(x, w, xdt), ydt)
+    say(f"  max-rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("m,n,k,xdt,ydt", [
+    (1, 300, 1152, "f16", "f32"),     # ragged n, odd G, one tile per matrix
+    (3, 257, 640, "bf16", "f32"),     # bf16 activations, ragged last tile
+    (4, 11008, 4096, "f16", "f16"),
+    (9, 1000, 2048, "f16", "bf16"),   # one row tile per matrix, 16 staged rows
+    (16, 5120, 4096, "f16", "f32"),   # two row tiles per matrix
+    (16, 11008, 4096, "f16", "f16"),  # the full gate/up shape: three row tiles per matrix
+    (16, 14336, 4096, "f16", "f32"),  # four row tiles per matrix
+    (1, 4096, 11008, "f16", "f32"),   # 86 groups
+    (40, 520, 1024, "f16", "f32"),    # prefill rows: two GEMMs
+])
+def test_gate_up_pair_parity(m, n, k, xdt, ydt):
+    """Both outputs of the pair against the oracle, and equal to the two
+    single-matrix calls bit for bit where the schedules match (every case
+    but m = 1 with 64 or more groups, where the single call takes two
+    groups per wave)."""
+    say(f"gate_up m={m} n={n} k={k} x={xdt} y={ydt}")
+    seed = 300 + m + n
+    x_np, _ = workloads.activations(m, k, seed, 0, dtype=xdt, outliers=(min(6, k // 128), 20.0, 80.0))
+    wg_np = workloads.weights(n, k, seed, 1, dtype=xdt)
+    wu_np = workloads.weights(n, k, seed, 2, dtype=xdt)
+    qg, qu = gpu_quantize_int4(dev(wg_np, xdt)), gpu_quantize_int4(dev(wu_np, xdt))
+    x = dev(x_np, xdt)
+    yg = torch.empty((m, n), dtype=torch_dtype(ydt), device="cuda")
+    yu = torch.empty_like(yg)
+    wq.wq_linear_w4a16_gate_up(x, qg, qu, yg, yu, act=0)
+    torch.cuda.synchronize()
+    g, u = to_np(yg), to_np(yu)
+    check_close(g, oracle_linear(x_np, wg_np, xdt), ydt)
+    check_close(u, oracle_linear(x_np, wu_np, xdt), ydt)
+    if not (m == 1 and k // 128 >= 64):
+        g1, _ = run_linear(x_np, wg_np, xdt, ydt, qw=qg)
+        u1, _ = run_linear(x_np, wu_np, xdt, ydt, qw=qu)
+        assert np.array_equal(g, g1) and np.array_equal(u, u1)
+
+
+@pytest.mark.parametrize("m,n,k,ydt", [
+    (1, 300, 1152, "f32"),
+    (5, 520, 2048, "bf16"),
+    (16, 11008, 4096, "f16"),         # the full gate/up shape
+    (16, 5120, 4096, "f32"),
+])
+def test_gate_up_swiglu_parity(m, n, k, ydt):
+    """silu(gate) * up against the oracle's fp64 product of its own fp64
+    projections."""
+    say(f"gate_up_swiglu m={m} n={n} k={k} y={ydt}")
+    seed = 400 + m + n
+    x_np, _ = workloads.activations(m, k, seed, 0, outliers=(min(6, k // 128), 20.0, 80.0))
+    wg_np = workloads.weights(n, k, seed, 1)
+    wu_np = workloads.weights(n, k, seed, 2)
+    qg, qu = gpu_quantize_int4(dev_f16(wg_np)), gpu_quantize_int4(dev_f16(wu_np))
+    y = torch.empty((m, n), dtype=torch_dtype(ydt), device="cuda")
+    wq.wq_linear_w4a16_gate_up(dev_f16(x_np), qg, qu, y, None, act=1)
+    torch.cuda.synchronize()
+    ref = linear.silu_gated(oracle_linear(x_np, wg_np, "f16"), oracle_linear(x_np, wu_np, "f16"))
+    rel = check_close(to_np(y), ref, ydt)
     say(f"  max-rel {rel:.2e}")
 
 

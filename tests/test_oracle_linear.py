@@ -3,6 +3,7 @@
 import struct
 
 import numpy as np
+import pytest
 
 from oracle import int4, linear
 from oracle.numerics import round_f16
@@ -56,3 +57,27 @@ def test_quantized_layer_error_is_small():
     y = linear.reference(d["x"], int4.dequantize(qw, s, z, 1024))
     ref = linear.reference(d["x"], d["w"])
     assert linear.max_rel_err(y, ref) < 0.1
+
+
+def test_silu_gated_closed_forms():
+    """sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 give exact values; the
+    identity silu(v) - silu(-v) = v (sigmoid(v) + sigmoid(-v) = 1) and the
+    two limits pin the sign of the exponent and the factor v."""
+    l3 = np.log(3.0)
+    assert linear.silu_gated(l3, 1.0) == pytest.approx(0.75 * l3, rel=1e-15)
+    assert linear.silu_gated(-l3, 1.0) == pytest.approx(-0.25 * l3, rel=1e-15)
+    assert linear.silu_gated(0.0, 5.0) == 0.0
+    v = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(linear.silu_gated(v, 1.0) - linear.silu_gated(-v, 1.0), v,
+                               rtol=0, atol=1e-12)
+    assert linear.silu_gated(40.0, 1.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(linear.silu_gated(-40.0, 1.0)) < 1e-15
+    assert linear.silu_gated(-1e4, 2.0) == 0.0          # exp overflow gives -0, not NaN
+
+
+def test_silu_gated_is_linear_in_up():
+    rng = np.random.default_rng(3)
+    g, u = rng.standard_normal(50), rng.standard_normal(50)
+    np.testing.assert_allclose(linear.silu_gated(g, 2.0 * u), 2.0 * linear.silu_gated(g, u),
+                               rtol=1e-15)
+    np.testing.assert_array_equal(linear.silu_gated(g, 0.0 * u), 0.0 * u)

@@ -17,15 +17,15 @@ import os
 __all__ = [
     "WqError", "QuantizedWeight", "F16", "BF16", "F32",
     "FMT_INT4_ASYM", "FMT_NF4", "FMT_INT8_SYM_ROW",
-    "wq_quantize_groupwise", "wq_pack_nf4", "wq_nf4_codebook",
+    "wq_quantize_groupwise", "wq_pack_nf4", "wq_nf4_codebook", "wq_pack_fp4", "wq_fp4_codebook",
     "wq_linear_w4a16_workspace", "wq_linear_w4a16", "wq_linear_w4a16_gate_up",
     "wq_int8_prepare_activations", "wq_linear_int8_decomp_workspace",
     "wq_linear_int8_decomp", "wq_dequantize", "wq_status_string",
-    "alloc_int4", "alloc_nf4", "alloc_int8", "library_path",
+    "alloc_int4", "alloc_nf4", "alloc_fp4", "alloc_int8", "library_path", "FMT_FP4",
 ]
 
 F16, BF16, F32 = 0, 1, 2
-FMT_INT4_ASYM, FMT_NF4, FMT_INT8_SYM_ROW = 0, 1, 2
+FMT_INT4_ASYM, FMT_NF4, FMT_INT8_SYM_ROW, FMT_FP4 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libwq.so")
@@ -70,6 +70,9 @@ def _load():
         "wq_pack_nf4": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
                                 c_vp, c_vp, c_vp, c_vp]),
         "wq_nf4_codebook": (c_i32, [ctypes.POINTER(ctypes.c_float)]),
+        "wq_pack_fp4": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                c_vp, c_vp, c_vp, c_vp]),
+        "wq_fp4_codebook": (c_i32, [ctypes.POINTER(ctypes.c_float)]),
         "wq_linear_w4a16_workspace": (ctypes.c_size_t, [c_i64, wp]),
         "wq_linear_w4a16": (c_i32, [c_vp, c_i32, c_i64, wp, c_vp, c_i32, c_vp,
                                     ctypes.c_size_t, c_vp]),
@@ -160,17 +163,21 @@ def alloc_int4(n, k, group=128, device="cuda"):
         torch.empty((n, (g + 1) // 2), dtype=torch.uint8, device=device))
 
 
-def alloc_nf4(n, k, block=64, double_quant=True, block2=256, device="cuda"):
+def alloc_nf4(n, k, block=64, double_quant=True, block2=256, device="cuda", fmt=FMT_NF4):
     import torch
     nb = n * k // block
     codes = torch.empty((n * k // 2,), dtype=torch.uint8, device=device)
     if double_quant:
-        return QuantizedWeight(FMT_NF4, n, k, block, codes,
+        return QuantizedWeight(fmt, n, k, block, codes,
                                torch.empty((nb,), dtype=torch.int8, device=device),
                                None, torch.empty(((nb + block2 - 1) // block2,),
                                                  dtype=torch.float32, device=device), block2)
-    return QuantizedWeight(FMT_NF4, n, k, block, codes,
+    return QuantizedWeight(fmt, n, k, block, codes,
                            torch.empty((nb,), dtype=torch.float32, device=device))
+
+
+def alloc_fp4(n, k, block=64, double_quant=True, block2=256, device="cuda"):
+    return alloc_nf4(n, k, block, double_quant, block2, device, fmt=FMT_FP4)
 
 
 def alloc_int8(n, k, device="cuda"):
@@ -192,6 +199,19 @@ def wq_pack_nf4(w, block, double_quant, block2, codes, absmax, absmax_scale=None
     st = _load().wq_pack_nf4(_ptr(w), _dt(w), n, k, block, 1 if double_quant else 0, block2,
                              _ptr(codes), _ptr(absmax), _ptr(absmax_scale), _stream(stream, w))
     _check(st, "wq_pack_nf4")
+
+
+def wq_pack_fp4(w, block, double_quant, block2, codes, absmax, absmax_scale=None, stream=None):
+    n, k = w.shape
+    st = _load().wq_pack_fp4(_ptr(w), _dt(w), n, k, block, 1 if double_quant else 0, block2,
+                             _ptr(codes), _ptr(absmax), _ptr(absmax_scale), _stream(stream, w))
+    _check(st, "wq_pack_fp4")
+
+
+def wq_fp4_codebook():
+    out = (ctypes.c_float * 16)()
+    _check(_load().wq_fp4_codebook(out), "wq_fp4_codebook")
+    return [float(v) for v in out]
 
 
 def wq_nf4_codebook():

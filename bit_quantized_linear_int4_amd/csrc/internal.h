@@ -55,7 +55,7 @@ hipError_t launch_quant_int8_rows(const void* w, int wdt, int64_t n, int64_t k,
                                   int8_t* codes, float* scales, hipStream_t s);
 hipError_t launch_pack_nf4(const void* w, int wdt, int64_t numel, int double_quant,
                            const float* thresholds15, uint8_t* codes, void* absmax,
-                           float* absmax_scale, hipStream_t s);
+                           float* absmax_scale, hipStream_t s, bool fp4 = false);
 
 struct W4Plan {
   int path;      // 1 = gemm (m > 16), 3 = streaming decode (m <= 16)
@@ -94,5 +94,9 @@ hipError_t launch_dequantize(const wq_weight* w, const float* levels16, void* ou
 // Host-side NF4 codebook (levels) and decision midpoints (thresholds).
 const float* nf4_levels();
 const float* nf4_thresholds();
+// FP4 (E2M1): 16 levels indexed by code, and the 7 magnitude midpoints
+// (padded to 15 with zeros)
+const float* fp4_levels();
+const float* fp4_thresholds();
 
 }  // namespace wq

@@ -7,6 +7,12 @@
 // quantizes the absmax values again: here to int8 per block of 256 absmax
 // values with one fp32 second-level scale (max/127).
 //
+// FP4 (same section 6.3 there; the E2M1 layout in "Inference & deployment
+// 05: quantized deployment compared", section 7.2) shares everything but the
+// codes: the sign of w/a goes to bit 3 and the magnitude code (bits 0-2, the
+// E2M1 exponent and mantissa) counts the 7 magnitude midpoints |w/a|
+// exceeds; an all-zero block gives code 0.
+//
 // One workgroup encodes one superblock of 256 blocks (16384 weights), so the
 // second-level scale needs no second pass: the 256 absmax values stay in LDS.
 // Eight lanes cover one 64-weight block (8 weights each, one 16-byte load,
@@ -20,7 +26,7 @@ struct Thresholds {
   float t[15];
 };
 
-template <int DT>
+template <int DT, bool FP4>
 __global__ __launch_bounds__(256) void pack_nf4_kernel(
     const uint16_t* __restrict__ w, int64_t nblocks, int double_quant, Thresholds th,
     uint32_t* __restrict__ codes, void* __restrict__ absmax, float* __restrict__ absmax_scale) {
@@ -55,12 +61,19 @@ __global__ __launch_bounds__(256) void pack_nf4_kernel(
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t c = 7;
+      uint32_t c = FP4 ? 0 : 7;
       if (a != 0.0f) {
         const float nv = __fdiv_rn(v[i], a);
         c = 0;
+        if constexpr (FP4) {
+          const float mag = fabsf(nv);
 #pragma unroll
-        for (int t = 0; t < 15; ++t) c += nv > th.t[t] ? 1u : 0u;
+          for (int t = 0; t < 7; ++t) c += mag > th.t[t] ? 1u : 0u;
+          c |= nv < 0.0f ? 8u : 0u;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 15; ++t) c += nv > th.t[t] ? 1u : 0u;
+        }
       }
       word |= c << (4 * i);
     }
@@ -95,17 +108,21 @@ __global__ __launch_bounds__(256) void pack_nf4_kernel(
 
 hipError_t launch_pack_nf4(const void* w, int wdt, int64_t numel, int double_quant,
                            const float* thresholds15, uint8_t* codes, void* absmax,
-                           float* absmax_scale, hipStream_t s) {
+                           float* absmax_scale, hipStream_t s, bool fp4) {
   Thresholds th;
   for (int i = 0; i < 15; ++i) th.t[i] = thresholds15[i];
   const int64_t nblocks = numel / 64;
   const dim3 grid((unsigned)((nblocks + 255) / 256));
   const uint16_t* wp = static_cast<const uint16_t*>(w);
   uint32_t* cw = reinterpret_cast<uint32_t*>(codes);
-  if (wdt == WQ_BF16)
-    pack_nf4_kernel<WQ_BF16><<<grid, 256, 0, s>>>(wp, nblocks, double_quant, th, cw, absmax, absmax_scale);
-  else
-    pack_nf4_kernel<WQ_F16><<<grid, 256, 0, s>>>(wp, nblocks, double_quant, th, cw, absmax, absmax_scale);
+#define WQ_PACK(DT, F) \
+  pack_nf4_kernel<DT, F><<<grid, 256, 0, s>>>(wp, nblocks, double_quant, th, cw, absmax, absmax_scale)
+  if (wdt == WQ_BF16) {
+    if (fp4) WQ_PACK(WQ_BF16, true); else WQ_PACK(WQ_BF16, false);
+  } else {
+    if (fp4) WQ_PACK(WQ_F16, true); else WQ_PACK(WQ_F16, false);
+  }
+#undef WQ_PACK
   return hipGetLastError();
 }
 

@@ -60,9 +60,37 @@ const Table& table() {
   return t;
 }
 
+// FP4: the E2M1 values of codes 0..15 (sign bit 3, exponent bits 2-1 with
+// bias 1, mantissa bit 0: magnitudes 0, 1/2, 1, 3/2, 2, 3, 4, 6) divided by
+// 6, and the fp32 midpoints between adjacent magnitudes.
+struct Fp4Table {
+  float levels[16];
+  float thresholds[15];
+  Fp4Table() {
+    for (int c = 0; c < 16; ++c) {
+      const int e = (c >> 1) & 3, m = c & 1;
+      const double mag = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+      const float v = (float)(mag / 6.0);
+      levels[c] = (c & 8) ? -v : v;
+    }
+    for (int i = 0; i < 15; ++i) thresholds[i] = 0.0f;
+    for (int i = 0; i < 7; ++i) {
+      volatile float s = levels[i] + levels[i + 1];  // fp32 sum
+      thresholds[i] = s * 0.5f;
+    }
+  }
+};
+
+const Fp4Table& fp4_table() {
+  static const Fp4Table t;
+  return t;
+}
+
 }  // namespace
 
 const float* nf4_levels() { return table().levels; }
 const float* nf4_thresholds() { return table().thresholds; }
+const float* fp4_levels() { return fp4_table().levels; }
+const float* fp4_thresholds() { return fp4_table().thresholds; }
 
 }  // namespace wq

@@ -42,6 +42,7 @@ wq_status check_weight(const wq_weight* w, bool linear_w4) {
       if (linear_w4 && w->group != 128) return WQ_ERR_UNSUPPORTED;
       return WQ_OK;
     case WQ_FMT_NF4:
+    case WQ_FMT_FP4:
       if (w->group != 64) return WQ_ERR_UNSUPPORTED;
       if (w->scales2 != nullptr && w->group2 != 256) return WQ_ERR_UNSUPPORTED;
       if ((w->n * w->k) % 64 != 0 || w->k % 8 != 0) return WQ_ERR_SHAPE;
@@ -56,6 +57,16 @@ wq_status check_weight(const wq_weight* w, bool linear_w4) {
     default:
       return WQ_ERR_UNSUPPORTED;
   }
+}
+
+// FP4 weights run the NF4 kernels with the FP4 level table.
+const float* levels_for(const wq_weight* w) {
+  return w->fmt == WQ_FMT_FP4 ? fp4_levels() : nf4_levels();
+}
+wq_weight kernel_view(const wq_weight* w) {
+  wq_weight c = *w;
+  if (c.fmt == WQ_FMT_FP4) c.fmt = WQ_FMT_NF4;
+  return c;
 }
 
 }  // namespace
@@ -73,6 +84,13 @@ const char* wq_status_string(int32_t status) {
     case WQ_ERR_HIP: return "WQ_ERR_HIP: kernel launch failed";
     default: return "unknown wq_status";
   }
+}
+
+wq_status wq_fp4_codebook(float* out) {
+  if (out == nullptr) return WQ_ERR_NULL;
+  const float* l = fp4_levels();
+  for (int i = 0; i < 16; ++i) out[i] = l[i];
+  return WQ_OK;
 }
 
 wq_status wq_nf4_codebook(float* out) {
@@ -108,9 +126,9 @@ wq_status wq_quantize_groupwise(const void* w, int32_t wdt, int64_t n, int64_t k
   return WQ_ERR_UNSUPPORTED;
 }
 
-wq_status wq_pack_nf4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t block,
-                      int32_t double_quant, int32_t block2, uint8_t* codes, void* absmax,
-                      float* absmax_scale, void* stream) {
+static wq_status pack_blockwise(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t block,
+                                int32_t double_quant, int32_t block2, uint8_t* codes,
+                                void* absmax, float* absmax_scale, void* stream, bool fp4) {
   if (w == nullptr || codes == nullptr || absmax == nullptr) return WQ_ERR_NULL;
   if (!is16(wdt)) return WQ_ERR_UNSUPPORTED;
   if (block != 64) return WQ_ERR_UNSUPPORTED;
@@ -124,13 +142,29 @@ wq_status wq_pack_nf4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t 
   }
   if (!sizes_ok(n, k) || (n * k) % 64 != 0) return WQ_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(codes, 16)) return WQ_ERR_ALIGN;
-  return hip_status(launch_pack_nf4(w, wdt, n * k, double_quant ? 1 : 0, nf4_thresholds(), codes,
-                                    absmax, absmax_scale, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_pack_nf4(w, wdt, n * k, double_quant ? 1 : 0,
+                                    fp4 ? fp4_thresholds() : nf4_thresholds(), codes, absmax,
+                                    absmax_scale, static_cast<hipStream_t>(stream), fp4));
+}
+
+wq_status wq_pack_nf4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t block,
+                      int32_t double_quant, int32_t block2, uint8_t* codes, void* absmax,
+                      float* absmax_scale, void* stream) {
+  return pack_blockwise(w, wdt, n, k, block, double_quant, block2, codes, absmax, absmax_scale,
+                        stream, false);
+}
+
+wq_status wq_pack_fp4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t block,
+                      int32_t double_quant, int32_t block2, uint8_t* codes, void* absmax,
+                      float* absmax_scale, void* stream) {
+  return pack_blockwise(w, wdt, n, k, block, double_quant, block2, codes, absmax, absmax_scale,
+                        stream, true);
 }
 
 size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w) {
   if (m < 1 || m >= kMaxDim || check_weight(w, true) != WQ_OK) return 0;
-  return plan_w4a16(m, w).ws;
+  const wq_weight kv = kernel_view(w);
+  return plan_w4a16(m, &kv).ws;
 }
 
 wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight* w, void* y,
@@ -143,12 +177,13 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight
     return WQ_ERR_SHAPE;
   if (w->k % 128 != 0) return WQ_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;
-  const W4Plan plan = plan_w4a16(m, w);
+  const wq_weight kv = kernel_view(w);
+  const W4Plan plan = plan_w4a16(m, &kv);
   if (plan.ws > 0) {
     if (workspace == nullptr || ws_bytes < plan.ws) return WQ_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return WQ_ERR_ALIGN;
   }
-  return hip_status(launch_w4a16(x, xdt, m, w, nf4_levels(), y, ydt, workspace, plan,
+  return hip_status(launch_w4a16(x, xdt, m, &kv, levels_for(w), y, ydt, workspace, plan,
                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -242,8 +277,9 @@ wq_status wq_dequantize(const wq_weight* w, void* out, int32_t odt, void* stream
   if (st != WQ_OK) return st;
   if (!is16(odt)) return WQ_ERR_UNSUPPORTED;
   if (!aligned(out, 16)) return WQ_ERR_ALIGN;
+  const wq_weight kv = kernel_view(w);
   return hip_status(
-      launch_dequantize(w, nf4_levels(), out, odt, static_cast<hipStream_t>(stream)));
+      launch_dequantize(&kv, levels_for(w), out, odt, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -64,7 +64,8 @@ typedef enum { WQ_F16 = 0, WQ_BF16 = 1, WQ_F32 = 2 } wq_dtype;
 typedef enum {
   WQ_FMT_INT4_ASYM = 0,   /* wq_quantize_groupwise(bits=4, symmetric=0)       */
   WQ_FMT_NF4 = 1,         /* wq_pack_nf4                                      */
-  WQ_FMT_INT8_SYM_ROW = 2 /* wq_quantize_groupwise(bits=8, symmetric=1, k)    */
+  WQ_FMT_INT8_SYM_ROW = 2,/* wq_quantize_groupwise(bits=8, symmetric=1, k)    */
+  WQ_FMT_FP4 = 3          /* wq_pack_fp4                                      */
 } wq_format;
 
 /*
@@ -85,6 +86,7 @@ typedef enum {
  *            else fp32 [n*k/group] absmax.
  *    scales2 fp32 [ceil(n*k/group / group2)] second-level scales, or NULL.
  *    group   NF4 block size (64); group2 the double-quant block (256).
+ *  fmt = WQ_FMT_FP4: the NF4 layout with E2M1 codes (see wq_pack_fp4).
  *  fmt = WQ_FMT_INT8_SYM_ROW:
  *    codes   int8 [n][k], 16-byte aligned; scales fp32 [n]; group = k.
  */
@@ -152,6 +154,27 @@ wq_status wq_pack_nf4(const void* w, int32_t wdt, int64_t n, int64_t k,
                       void* stream);
 
 /*
+ * FP4 blockwise quantization, the FP4 variant of the NF4 path ([P1] 6.3
+ * names bitsandbytes' NF4 and FP4 formats; the E2M1 layout, sign bit,
+ * 2-bit exponent, 1-bit mantissa, is [P5] 7.2).  Arguments, blocks, absmax
+ * and double quantization exactly as wq_pack_nf4; only the codes differ:
+ *   code bit 3 = (w/a < 0); bits 0-2 = number of the 7 midpoints between
+ *   adjacent E2M1 magnitudes {0, 1/2, 1, 3/2, 2, 3, 4, 6}/6 that |w/a|
+ *   exceeds (nearest magnitude, ties to the lower); a == 0 gives code 0.
+ * Code c decodes to wq_fp4_codebook()[c] * absmax (code 8 is -0).
+ */
+wq_status wq_pack_fp4(const void* w, int32_t wdt, int64_t n, int64_t k,
+                      int32_t block, int32_t double_quant, int32_t block2,
+                      uint8_t* codes, void* absmax, float* absmax_scale,
+                      void* stream);
+
+/*
+ * The FP4 codebook (host call, no GPU): out[c] = E2M1 value of code c / 6
+ * in fp32, exponent bias 1 (out[7] = 1, out[15] = -1, out[8] = -0).
+ */
+wq_status wq_fp4_codebook(float* out);
+
+/*
  * The NF4 codebook the library uses (host call, no GPU): 16 fp32 levels,
  * ascending, out[0] = -1, out[7] = 0, out[15] = 1.  Level i > 7 is
  * PhiInv(p_i)/PhiInv(31/32) for p_i = 1/2 + (31/32 - 1/2) (i-7)/8, level
@@ -174,14 +197,14 @@ size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w);
  * with fp32 accumulation, [P1] section 5 opening, [P1] 6.2, [P2] 十一).
  *
  *   y[i][j] = sum_c x[i][c] * w_hat[j][c]
- *     INT4: w_hat = (q - z) * s, NF4: w_hat = L[code] * a_hat,
- *     with fp32 accumulation.
+ *     INT4: w_hat = (q - z) * s, NF4 and FP4: w_hat = L[code] * a_hat
+ *     (L the format's codebook), with fp32 accumulation.
  *
  * Decode-shaped calls (m <= 16) run a bandwidth-bound dequant-GEMV; larger
  * m runs an MFMA dequant-GEMM (the GEMV / GEMM kernel versions of [P1] 4.3).
  *
  * x: xdt in {WQ_F16, WQ_BF16}, [m][k], 16-byte aligned.  w: fmt INT4_ASYM
- * (group 128) or NF4 (block 64).  y: ydt in {F16, BF16, F32}, [m][n].
+ * (group 128), NF4 or FP4 (block 64).  y: ydt in {F16, BF16, F32}, [m][n].
  * workspace: at least wq_linear_w4a16_workspace(m, w) bytes, 256-byte
  * aligned (may be NULL when that is 0).  m >= 1; k % 128 == 0.
  */
@@ -251,7 +274,7 @@ wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w,
 
 /*
  * Dequantize a whole weight into 16-bit values (a test and debugging hook):
- * INT4: fp(q - z) * s rounded to odt; NF4: L[code] * a_hat rounded to odt;
+ * INT4: fp(q - z) * s rounded to odt; NF4, FP4: L[code] * a_hat rounded to odt;
  * INT8: fp32(q) * s rounded to odt.  out: odt in {F16, BF16} [n][k].
  */
 wq_status wq_dequantize(const wq_weight* w, void* out, int32_t odt, void* stream);

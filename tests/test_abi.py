@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import bit_quantized_linear_int4_amd as wq
-from oracle import nf4
+from oracle import fp4, nf4
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wq.h")
@@ -54,6 +54,15 @@ def test_library_codebook_matches_oracle():
     assert np.array_equal(lib_levels, nf4.codebook())
 
 
+def test_library_fp4_codebook_matches_oracle():
+    """The library's FP4 table (E2M1 values / 6, by code) equals the
+    oracle's in fp32, including the sign of code 8's zero."""
+    lib_levels = np.array(wq.wq_fp4_codebook(), dtype=np.float32)
+    ref = fp4.codebook()
+    assert np.array_equal(lib_levels, ref)
+    assert np.array_equal(np.signbit(lib_levels), np.signbit(ref))
+
+
 # fake device addresses: never dereferenced, because validation fails first
 A16 = 0x10000
 ODD = 0x10001
@@ -89,8 +98,9 @@ def test_quantize_argument_errors():
     assert call(bits=8, sym=1, group=256) == UNSUP  # zeros must be NULL
 
 
-def test_pack_nf4_argument_errors():
-    p = _lib().wq_pack_nf4
+@pytest.mark.parametrize("entry", ["wq_pack_nf4", "wq_pack_fp4"])
+def test_pack_nf4_argument_errors(entry):
+    p = getattr(_lib(), entry)
 
     def call(w=A16, wdt=wq.BF16, n=4, k=256, block=64, dq=1, block2=256, codes=A16,
              absmax=A16, scale2=A16):

@@ -13,7 +13,7 @@ import torch
 
 import bit_quantized_linear_int4_amd as wq
 import workloads
-from oracle import linear, nf4
+from oracle import fp4, linear, nf4
 from gpu_util import check_close, dev, host16, say, to_np, torch_dtype
 
 pytestmark = pytest.mark.gpu
@@ -118,3 +118,69 @@ def test_linear_nf4_full_layer():
         ref = oracle_y(d["x"][m], d["w"], "bf16", True, rows)
         rel = check_close(y if rows is None else y[rows], ref, "f32")
         say(f"  m={m} max-rel {rel:.2e}")
+
+
+# ---------------------------------------------------------------- FP4 (E2M1)
+
+def gpu_pack_fp4(w_dev, double_quant=True):
+    n, k = w_dev.shape
+    qw = wq.alloc_fp4(n, k, double_quant=double_quant)
+    wq.wq_pack_fp4(w_dev, 64, double_quant, 256, qw.codes, qw.scales, qw.scales2)
+    return qw
+
+
+@pytest.mark.parametrize("n,k,dtype,dq", [
+    (64, 512, "bf16", True),
+    (37, 640, "f16", False),       # numel not a multiple of 256 blocks
+    (14336, 4096, "bf16", True),   # the 8B-shaped layer
+])
+def test_pack_fp4_bitexact(n, k, dtype, dq):
+    say(f"pack_fp4 n={n} k={k} dtype={dtype} dq={dq}")
+    w = workloads.weights(n, k, 50 + n, 1, dtype=dtype)
+    if n == 64:
+        wv = host16(w, dtype).copy()
+        wv[0, :64] = 0                        # all-zero block -> code 0
+        wv[1, :64] = np.linspace(-1, 1, 64)    # exact +-absmax -> codes 15, 7
+        w = workloads.to_bf16_bits(wv) if dtype == "bf16" else wv.astype(np.float16)
+    qw = gpu_pack_fp4(dev(w, dtype), dq)
+    torch.cuda.synchronize()
+    ref_codes, ref_a, ref_c2 = fp4.quantize(host16(w, dtype), double_quant=dq)
+    assert np.array_equal(qw.codes.cpu().numpy(), ref_codes)
+    assert np.array_equal(qw.scales.cpu().numpy(), ref_a)
+    if dq:
+        assert np.array_equal(qw.scales2.cpu().numpy(), ref_c2)
+
+
+@pytest.mark.parametrize("dq,odt", [(True, "bf16"), (False, "f16")])
+def test_dequantize_fp4_bitexact(dq, odt):
+    say(f"dequantize_fp4 dq={dq} odt={odt}")
+    n, k = 40, 1024
+    w = workloads.weights(n, k, 78, 1, dtype="bf16")
+    qw = gpu_pack_fp4(dev(w, "bf16"), dq)
+    out = torch.empty((n, k), dtype=torch_dtype(odt), device="cuda")
+    wq.wq_dequantize(qw, out)
+    torch.cuda.synchronize()
+    c, a, c2 = fp4.quantize(host16(w, "bf16"), double_quant=dq)
+    assert np.array_equal(to_np(out), fp4.dequantize(c, a, c2, (n, k), out_dtype=odt))
+
+
+@pytest.mark.parametrize("m,n,k,xdt,ydt,dq", [
+    (1, 300, 1152, "bf16", "f32", True),
+    (4, 272, 640, "f16", "f32", False),
+    (16, 512, 2048, "bf16", "f32", True),
+    (40, 300, 1152, "bf16", "f32", True),
+    (512, 1024, 4096, "bf16", "f32", True),
+])
+def test_linear_fp4_parity(m, n, k, xdt, ydt, dq):
+    say(f"linear_fp4 m={m} n={n} k={k} x={xdt} y={ydt} dq={dq}")
+    seed = 500 + m + n
+    x, _ = workloads.activations(m, k, seed, 0, dtype=xdt)
+    w = workloads.weights(n, k, seed, 1, dtype=xdt)
+    qw = gpu_pack_fp4(dev(w, xdt), dq)
+    y = torch.empty((m, n), dtype=torch_dtype(ydt), device="cuda")
+    wq.wq_linear_w4a16(dev(x, xdt), qw, y, None)
+    torch.cuda.synchronize()
+    c, a, c2 = fp4.quantize(host16(w, xdt), double_quant=dq)
+    wh = fp4.dequantize(c, a, c2, (n, k), out_dtype=xdt)
+    rel = check_close(to_np(y), linear.reference(host16(x, xdt), wh), ydt)
+    say(f"  max-rel {rel:.2e}")

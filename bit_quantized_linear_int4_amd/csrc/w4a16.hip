@@ -96,7 +96,8 @@ struct SkinnyArgs {
   const void* scales;        // INT4: fp16 [n][G]; NF4: int8 or fp32 absmax
   const uint8_t* zeros;      // INT4 only
   const float* scales2;      // NF4 double-quant second level, or nullptr
-  int m, n, k, G, zb;        // zb = bytes per row of zeros
+  int m, n, k, G, zb;        // G = k/128 units of 128; zb = bytes per row of zeros
+  int GS, sub;               // INT4: groups per row (k/group), groups per unit (1, 2, 4)
   float* partial;            // [splits][m][n] when the K range is split
   void* y;
   // second INT4 matrix of a gate/up pair (same n, k; same x), its output,
@@ -262,13 +263,16 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, kq = lane >> 4;
+  // INT4 group of this lane's codes: lane kq holds quarter kq (32 codes) of
+  // each unit of 128, i.e. group unit * sub + lq
+  const int lq = (kq * a.sub) >> 2;
   const int ntiles = (a.n + 15) / 16;
-  // this workgroup's K slice: groups [gbeg, gend)
+  // this workgroup's K slice: units [gbeg, gend)
   const int gbeg = (int)blockIdx.y * kslice;
   const int gend = min(a.G, gbeg + kslice);
   uint4_t* const ring = dsm + wave * NBUF * XS;
   // staged scales / zeros: per tile SCB and ZCB bytes (multiples of 1 KB)
-  const int SCB = (32 * a.G + 1023) / 1024 * 1024;
+  const int SCB = (32 * a.GS + 1023) / 1024 * 1024;
   const int ZCB = (16 * a.zb + 1023) / 1024 * 1024;
   uint8_t* const scl = reinterpret_cast<uint8_t*>(dsm + NW * NBUF * XS);
   uint8_t* const zcl = scl + TPG * SCB;
@@ -290,13 +294,13 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     // 1 KB direct loads of the tiles' scale and zero rows, spread over the
     // waves; chunks past the end of a buffer reload its last 16 bytes
     const int nsc = SCB / 1024, nzc = ZCB / 1024, per = nsc + nzc;
-    const int64_t sbytes = (int64_t)a.n * a.G * 2, zbytes = (int64_t)a.n * a.zb;
+    const int64_t sbytes = (int64_t)a.n * a.GS * 2, zbytes = (int64_t)a.n * a.zb;
     for (int i = wave; i < TPG * per; i += NW) {
       const int t = i / per, j = i % per;
       const int tile = tile_of(t);
       const bool isz = j >= nsc;
       const int jj = isz ? j - nsc : j;
-      const int64_t off = (int64_t)tile * 16 * (isz ? a.zb : 2 * a.G) + jj * 1024 + lane * 16;
+      const int64_t off = (int64_t)tile * 16 * (isz ? a.zb : 2 * a.GS) + jj * 1024 + lane * 16;
       const int64_t lim = (isz ? zbytes : sbytes) - 16;
       const uint8_t* zsrc = second(t) ? a.zeros_b : a.zeros;
       const uint8_t* ssrc = static_cast<const uint8_t*>(second(t) ? a.scales_b : a.scales);
@@ -353,8 +357,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
         if constexpr (SZL) {
         } else if constexpr (FMT == WQ_FMT_INT4_ASYM) {
           const uint16_t* sp = static_cast<const uint16_t*>(second(t) ? a.scales_b : a.scales);
-          sv[b][t][u] = f16_bits_to_f32(sp[(int64_t)row * a.G + g]);
-          zv[b][t][u] = (second(t) ? a.zeros_b : a.zeros)[(int64_t)row * a.zb + (g >> 1)];
+          const int gq = g * a.sub + lq;
+          sv[b][t][u] = f16_bits_to_f32(sp[(int64_t)row * a.GS + gq]);
+          zv[b][t][u] = (second(t) ? a.zeros_b : a.zeros)[(int64_t)row * a.zb + (gq >> 1)];
         } else {
           // the first-level absmax (int8 code or fp32) and the second-level
           // scale (a harmless reload of element 0 without double quantization)
@@ -418,14 +423,15 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
 #pragma unroll
     for (int u = 0; u < GPP; ++u) {
       const int g = gbeg + p * CG + wave * GPP + u;
+      const int gq = g * a.sub + lq;            // this lane's INT4 group
       if (g < gend) {
         if constexpr (SZL) {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
             if constexpr (CRING) wv[b][t][u] = wring[((b * TPG + t) * GPP + u) * 64 + lane];
-            const uint16_t sc = *reinterpret_cast<const uint16_t*>(scl + t * SCB + (nl * a.G + g) * 2);
+            const uint16_t sc = *reinterpret_cast<const uint16_t*>(scl + t * SCB + (nl * a.GS + gq) * 2);
             sv[b][t][u] = f16_bits_to_f32(sc);
-            zv[b][t][u] = zcl[t * ZCB + nl * a.zb + (g >> 1)];
+            zv[b][t][u] = zcl[t * ZCB + nl * a.zb + (gq >> 1)];
           }
         }
         uint4_t A[4];
@@ -435,18 +441,50 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
           A[j] = FAST ? perm_x(v) : v;
         }
         if constexpr (FAST) {
-          float4_t X = {0.f, 0.f, 0.f, 0.f};
+          if (a.sub == 1) {
+            // one group per unit: the MFMA sums x (1024 + q) over the unit,
+            // then s (acc - (1024 + z) X) removes bias and zero point
+            float4_t X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) X = mfma16<XDT>(A[j], ones, X);
+            for (int j = 0; j < 4; ++j) X = mfma16<XDT>(A[j], ones, X);
 #pragma unroll
-          for (int t = 0; t < TPG; ++t) {
-            float4_t tmp = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < TPG; ++t) {
+              float4_t tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tmp = mfma16<XDT>(A[j], unpack_biased_f16(wv[b][t][u][j]), tmp);
-            const uint32_t z = (g & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u);
-            const float zb = 1024.0f + (float)z;
+              for (int j = 0; j < 4; ++j) tmp = mfma16<XDT>(A[j], unpack_biased_f16(wv[b][t][u][j]), tmp);
+              const uint32_t z = (gq & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u);
+              const float zb = 1024.0f + (float)z;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(fmaf(-zb, X[e], tmp[e]), sv[b][t][u], acc[t][e]);
+              for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(fmaf(-zb, X[e], tmp[e]), sv[b][t][u], acc[t][e]);
+            }
+          } else {
+            // groups of 64 or 32: an MFMA sums over every quarter of the unit,
+            // so each lane dequantizes exactly with its own group's scale and
+            // zero point: (1024 + q) - (1024 + z) = q - z, times s, rounded
+            // once to fp16 -- the weight the method defines
+#pragma unroll
+            for (int t = 0; t < TPG; ++t) {
+              const uint32_t z = (gq & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u);
+              const _Float16 nz = (_Float16)(-(1024.0f + (float)z));
+              const _Float16 sc = (_Float16)sv[b][t][u];
+              const half2_t nz2 = {nz, nz}, s2 = {sc, sc};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint4_t bq = unpack_biased_f16(wv[b][t][u][j]);
+                uint4_t bw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  half2_t h;
+                  const uint32_t ue = bq[e];
+                  __builtin_memcpy(&h, &ue, 4);
+                  h = (h + nz2) * s2;
+                  uint32_t o;
+                  __builtin_memcpy(&o, &h, 4);
+                  bw[e] = o;
+                }
+                acc[t] = mfma16<XDT>(A[j], bw, acc[t]);
+              }
+            }
           }
         } else {
 #pragma unroll
@@ -455,7 +493,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
             for (int j = 0; j < 4; ++j) {
               uint4_t bw;
               if constexpr (FMT == WQ_FMT_INT4_ASYM) {
-                const float z = (float)((g & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u));
+                const float z = (float)((gq & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u));
                 bw = dequant_int4_word<XDT>(wv[b][t][u][j], z, sv[b][t][u]);
               } else {
                 bw = dequant_nf4_word<XDT>(wv[b][t][u][j], lut, sv[b][t][u]);
@@ -553,7 +591,8 @@ struct GemmArgs {
   const void* scales;
   const uint8_t* zeros;
   const float* scales2;
-  int m, n, k, G, zb;
+  int m, n, k, G, zb;        // G = k/128 units of 128; zb = bytes per row of zeros
+  int GS, sub;               // INT4: groups per row (k/group), groups per unit (1, 2, 4)
   void* y;
 };
 
@@ -563,8 +602,8 @@ template <int FMT, int XDT>
 __device__ __forceinline__ void dequant32(const GemmArgs& a, const float* lut, int r, int c0,
                                           uint4_t wv, uint32_t (&out)[16]) {
   if constexpr (FMT == WQ_FMT_INT4_ASYM) {
-    const int g = c0 >> 7;
-    const float s = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)r * a.G + g]);
+    const int g = c0 / (128 / a.sub);               // a 32-chunk lies in one group
+    const float s = f16_bits_to_f32(static_cast<const uint16_t*>(a.scales)[(int64_t)r * a.GS + g]);
     const uint8_t zbyte = a.zeros[(int64_t)r * a.zb + (g >> 1)];
     const float z = (float)((g & 1) ? (zbyte >> 4) : (zbyte & 15));
 #pragma unroll
@@ -735,7 +774,6 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
   constexpr int WBUF = BN * 4;                   // 16-byte chunks per code buffer
   constexpr int XI = XBUF / 64 / NW;             // activation loads per wave and group
   constexpr int WI = WBUF / 64 / NW;             // code loads per wave and group
-  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   __shared__ uint4_t xr[2 * XBUF];
   __shared__ uint4_t wr[3 * WBUF];
   __shared__ __attribute__((aligned(16))) uint8_t scl[kGemmScaleBytes];
@@ -760,19 +798,20 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
   const int grp = tile / (GM * ntn), gm = min(ntm - grp * GM, GM);
   const int tr = tile - grp * GM * ntn;
   const int m0 = (grp * GM + tr % gm) * BM, n0 = (tr / gm) * BN;
-  const int G = a.G;
-  const int SCB = (BN * G * 2 + 1023) / 1024 * 1024;
+  const int G = a.G, GS = a.GS;                  // units of 128; groups per row
+  const int SCB = (BN * GS * 2 + 1023) / 1024 * 1024;
   const int ZCB = (BN * a.zb + 1023) / 1024 * 1024;
+  const int lq = (kq * a.sub) >> 2;              // this lane's group within a unit
 
   // staged scales and zero points of rows n0 .. n0+255 (clamped at the end
   // of the buffers; rows past n are never stored)
   {
     const int nsc = SCB / 1024, nzc = ZCB / 1024;
-    const int64_t sbytes = (int64_t)a.n * G * 2, zbytes = (int64_t)a.n * a.zb;
+    const int64_t sbytes = (int64_t)a.n * GS * 2, zbytes = (int64_t)a.n * a.zb;
     for (int i = wave; i < nsc + nzc; i += NW) {
       const bool isz = i >= nsc;
       const int j = isz ? i - nsc : i;
-      const int64_t off = (int64_t)n0 * (isz ? a.zb : 2 * G) + j * 1024 + lane * 16;
+      const int64_t off = (int64_t)n0 * (isz ? a.zb : 2 * GS) + j * 1024 + lane * 16;
       const uint8_t* src = (isz ? a.zeros : static_cast<const uint8_t*>(a.scales)) +
                            min(off, (isz ? zbytes : sbytes) - 16);
       lds_dma16(src, (lds_void_t*)((isz ? zcl : scl) + j * 1024));
@@ -842,10 +881,11 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
     for (int j = 0; j < NF; ++j) {
       const int r = wn * 16 * NF + j * 16 + nl;
       wv[j] = wcur[r * 4 + (kq ^ ((r >> 2) & 3))];
+      const int gq = g * a.sub + lq;
       _Float16 sc16;
-      __builtin_memcpy(&sc16, scl + (r * G + g) * 2, 2);
-      const uint32_t zb = zcl[r * a.zb + (g >> 1)];
-      const float z = (float)((g & 1) ? (zb >> 4) : (zb & 15u));
+      __builtin_memcpy(&sc16, scl + (r * GS + gq) * 2, 2);
+      const uint32_t zb = zcl[r * a.zb + (gq >> 1)];
+      const float z = (float)((gq & 1) ? (zb >> 4) : (zb & 15u));
       s2[j] = half2_t{sc16, sc16};
       nz2[j] = half2_t{(_Float16)(-(1024.0f + z)), (_Float16)(-(64.0f + z))};
     }
@@ -908,13 +948,18 @@ hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+// INT4 groups per row (k / group); other formats: the units of 128.
+inline int int4_groups(const wq_weight* w) {
+  return (int)(w->fmt == WQ_FMT_INT4_ASYM ? w->k / w->group : w->k / 128);
+}
+
 // ---------------------------------------------------------------- launch
 // Streaming decode configurations: NW, TPG, GPP, MP, NBUF.
 template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL,
           bool DUAL = false>
 hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
   auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL, DUAL>;
-  const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, DUAL, a.G, a.zb);
+  const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, DUAL, a.GS, a.zb);
   if (a.m > MP) return hipErrorInvalidValue;   // rows past MP are never staged
   if (lds > 160 * 1024 - 256) return hipErrorInvalidConfiguration;
   // raise the dynamic LDS limit of this instantiation when a launch needs
@@ -1004,9 +1049,11 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
     a.n = (int)w->n;
     a.k = (int)w->k;
     a.G = (int)(w->k / 128);
-    a.zb = (a.G + 1) / 2;
+    a.GS = int4_groups(w);
+    a.sub = a.GS / a.G;
+    a.zb = (a.GS + 1) / 2;
     a.y = y;
-    if (XDT == WQ_F16 && w->fmt == WQ_FMT_INT4_ASYM && p.szl && a.G <= kGemmMaxGroups)
+    if (XDT == WQ_F16 && w->fmt == WQ_FMT_INT4_ASYM && p.szl && a.GS <= kGemmMaxGroups)
       return launch_gemm_i4<YDT>(a, s);
     const dim3 grid((unsigned)((w->n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
     if (w->fmt == WQ_FMT_NF4)
@@ -1025,7 +1072,9 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
   a.n = (int)w->n;
   a.k = (int)w->k;
   a.G = (int)(w->k / 128);
-  a.zb = (a.G + 1) / 2;
+  a.GS = int4_groups(w);
+  a.sub = a.GS / a.G;
+  a.zb = (a.GS + 1) / 2;
   a.y = y;
   a.partial = static_cast<float*>(ws);
   return w->fmt == WQ_FMT_NF4 ? launch_stream<XDT, YDT, WQ_FMT_NF4>(a, lv, p, s)
@@ -1045,7 +1094,9 @@ hipError_t launch_pair_typed(const void* x, int64_t m, const wq_weight* wg, cons
   a.n = (int)wg->n;
   a.k = (int)wg->k;
   a.G = (int)(wg->k / 128);
-  a.zb = (a.G + 1) / 2;
+  a.GS = int4_groups(wg);
+  a.sub = a.GS / a.G;
+  a.zb = (a.GS + 1) / 2;
   a.y = yg;
   a.codes_b = static_cast<const uint32_t*>(wu->codes);
   a.scales_b = wu->scales;
@@ -1087,9 +1138,10 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   p.phases = 1;
   p.grid = 0;
   p.ws = 0;
+  const int64_t GS = int4_groups(w);
   p.szl = w->fmt == WQ_FMT_INT4_ASYM && ((uintptr_t)w->scales % 16) == 0 &&
-          ((uintptr_t)w->zeros % 16) == 0 && (w->n * (w->k / 128) * 2) % 16 == 0 &&
-          (w->n * ((w->k / 128 + 1) / 2)) % 16 == 0;
+          ((uintptr_t)w->zeros % 16) == 0 && (w->n * GS * 2) % 16 == 0 &&
+          (w->n * ((GS + 1) / 2)) % 16 == 0;
   if (p.path == 1) return p;
   const int64_t G = w->k / 128;
   const int64_t ntiles = (w->n + 15) / 16;
@@ -1139,7 +1191,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
       // staged scales must fit beside the activation ring
       if (p.szl) {
         const size_t lds = stream_lds_bytes(sc.nw, sc.tpg, sc.gpp, sc.mp, sc.nbuf, true, false,
-                                            (int)G, (int)((G + 1) / 2));
+                                            (int)GS, (int)((GS + 1) / 2));
         if (lds > 160 * 1024 - 256) p.szl = false;
       }
     }
@@ -1186,8 +1238,9 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
       p.phases = (int)((G + pc.nw * pc.gpp - 1) / (pc.nw * pc.gpp));
       p.grid = (int)((ntiles + pc.tpg / 2 - 1) / (pc.tpg / 2));
       p.ws = 0;
-      if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true, (int)G,
-                                    (int)((G + 1) / 2)) > 160 * 1024 - 256)
+      const int64_t GSp = int4_groups(wg);
+      if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true, (int)GSp,
+                                    (int)((GSp + 1) / 2)) > 160 * 1024 - 256)
         p.szl = false;
     }
   return p;

@@ -39,7 +39,6 @@ wq_status check_weight(const wq_weight* w, bool linear_w4) {
       if (w->group != 32 && w->group != 64 && w->group != 128) return WQ_ERR_UNSUPPORTED;
       if (w->k % w->group != 0 || w->k % 8 != 0) return WQ_ERR_SHAPE;
       if (!aligned(w->scales, 2)) return WQ_ERR_ALIGN;
-      if (linear_w4 && w->group != 128) return WQ_ERR_UNSUPPORTED;
       return WQ_OK;
     case WQ_FMT_NF4:
     case WQ_FMT_FP4:
@@ -199,7 +198,9 @@ wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
   if (st != WQ_OK) return st;
   if (w_gate->fmt != WQ_FMT_INT4_ASYM || w_up->fmt != WQ_FMT_INT4_ASYM) return WQ_ERR_UNSUPPORTED;
   if (!is16(xdt) || !is_out(ydt)) return WQ_ERR_UNSUPPORTED;
-  if (w_gate->n != w_up->n || w_gate->k != w_up->k || w_gate->k % 128 != 0) return WQ_ERR_SHAPE;
+  if (w_gate->n != w_up->n || w_gate->k != w_up->k || w_gate->group != w_up->group ||
+      w_gate->k % 128 != 0)
+    return WQ_ERR_SHAPE;
   if (m < 1 || m >= kMaxDim || m > kMaxElems / w_gate->k || m > kMaxElems / w_gate->n)
     return WQ_ERR_SHAPE;
   if (act == 1 && m > 16) return WQ_ERR_UNSUPPORTED;

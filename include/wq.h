@@ -204,7 +204,8 @@ size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w);
  * m runs an MFMA dequant-GEMM (the GEMV / GEMM kernel versions of [P1] 4.3).
  *
  * x: xdt in {WQ_F16, WQ_BF16}, [m][k], 16-byte aligned.  w: fmt INT4_ASYM
- * (group 128), NF4 or FP4 (block 64).  y: ydt in {F16, BF16, F32}, [m][n].
+ * (group 128, 64 or 32: the group-size knob of [P5] 2.2 and [P1] 3.2), NF4
+ * or FP4 (block 64).  y: ydt in {F16, BF16, F32}, [m][n].
  * workspace: at least wq_linear_w4a16_workspace(m, w) bytes, 256-byte
  * aligned (may be NULL when that is 0).  m >= 1; k % 128 == 0.
  */
@@ -225,9 +226,9 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m,
  * once; larger m runs the two GEMMs (act = 1 is decode only).
  *
  * x: xdt in {WQ_F16, WQ_BF16}, [m][k], 16-byte aligned.  w_gate, w_up:
- * INT4_ASYM group 128 with equal n and k.  y_gate, y_up: ydt in
+ * INT4_ASYM (group 128, 64 or 32) with equal n and k.  y_gate, y_up: ydt in
  * {F16, BF16, F32}, [m][n] each (y_up may be NULL when act = 1).
- * Errors: WQ_ERR_SHAPE when n or k differ; WQ_ERR_UNSUPPORTED for NF4,
+ * Errors: WQ_ERR_SHAPE when n, k or the group size differ; WQ_ERR_UNSUPPORTED for NF4,
  * act outside {0, 1}, or act = 1 with m > 16.  No workspace.
  */
 wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,

@@ -140,6 +140,7 @@ def test_gate_up_argument_errors():
     assert call(act=1, m=17) == UNSUP                 # the SiLU product is decode only
     assert call(wu=_weight(n=128)) == SHAPE           # the pair shares n and k
     assert call(wu=_weight(k=384)) == SHAPE
+    assert call(wu=_weight(group=64)) == SHAPE        # and the group size
     assert call(m=0) == SHAPE
     assert call(m=1 << 23) == SHAPE
     assert call(wg=_weight(fmt=wq.FMT_NF4, group=64, zeros=None)) == UNSUP
@@ -160,7 +161,7 @@ def test_linear_w4a16_argument_errors():
     assert call(w=_weight(zeros=None)) == NULL
     assert call(m=0) == SHAPE
     assert call(w=_weight(k=200, group=8)) == UNSUP
-    assert call(w=_weight(group=64)) == UNSUP     # linear runs group 128
+    assert call(w=_weight(group=16)) == UNSUP     # groups of 128, 64 or 32
     assert call(w=_weight(k=136)) == SHAPE
     assert call(x=ODD) == ALIGN
     assert call(w=_weight(codes=A16 + 8)) == ALIGN

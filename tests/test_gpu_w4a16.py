@@ -100,9 +100,9 @@ def run_linear(x_np, w_np, xdt, ydt, qw=None):
     return to_np(y), qw
 
 
-def oracle_linear(x_np, w_np, xdt, rows=None):
+def oracle_linear(x_np, w_np, xdt, rows=None, group=128):
     n, k = w_np.shape
-    wh = int4.dequantize(*int4.quantize(host16(w_np, xdt)), k, out_dtype=xdt)
+    wh = int4.dequantize(*int4.quantize(host16(w_np, xdt), group), k, group=group, out_dtype=xdt)
     xs = host16(x_np, xdt)
     if rows is not None:
         xs = xs[rows]
@@ -213,6 +213,54 @@ def test_gate_up_swiglu_parity(m, n, k, ydt):
     ref = linear.silu_gated(oracle_linear(x_np, wg_np, "f16"), oracle_linear(x_np, wu_np, "f16"))
     rel = check_close(to_np(y), ref, ydt)
     say(f"  max-rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("m,n,k,xdt,ydt,group", [
+    (1, 300, 1152, "f16", "f32", 64),     # scales not stageable (n * zb % 16 != 0)
+    (1, 4096, 4096, "f16", "f16", 32),
+    (4, 11008, 4096, "f16", "f32", 64),
+    (16, 11008, 4096, "f16", "f16", 32),  # three row tiles, staged scales
+    (16, 4096, 11008, "f16", "f32", 64),  # 172 groups per row
+    (3, 257, 640, "bf16", "f32", 32),     # bf16: the exact per-word decoder
+    (9, 1000, 2048, "bf16", "bf16", 64),
+    (40, 520, 1024, "f16", "f32", 64),    # GEMM with staged scales (16 groups)
+    (300, 1024, 2048, "f16", "f16", 32),  # GEMM, 64 groups: the staging limit
+    (130, 272, 4096, "f16", "f32", 32),   # 128 groups: the generic GEMM
+    (200, 520, 1024, "bf16", "f32", 64),
+])
+def test_linear_group_sizes(m, n, k, xdt, ydt, group):
+    """Groups of 64 and 32 ([P5] 2.2 group-wise granularity, the group-size
+    knob): every decode and GEMM path against the oracle with the same
+    groups."""
+    say(f"linear_group m={m} n={n} k={k} x={xdt} y={ydt} group={group}")
+    seed = 600 + m + n + group
+    x, _ = workloads.activations(m, k, seed, 0, dtype=xdt, outliers=(min(6, k // 128), 20.0, 80.0))
+    w = workloads.weights(n, k, seed, 1, dtype=xdt)
+    qw = gpu_quantize_int4(dev(w, xdt), group)
+    y, _ = run_linear(x, w, xdt, ydt, qw=qw)
+    rel = check_close(y, oracle_linear(x, w, xdt, group=group), ydt)
+    say(f"  max-rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("m,n,k,group,act", [(16, 5120, 4096, 64, 0), (1, 300, 1152, 32, 1)])
+def test_gate_up_group_sizes(m, n, k, group, act):
+    say(f"gate_up_group m={m} n={n} k={k} group={group} act={act}")
+    seed = 700 + m + n
+    x_np, _ = workloads.activations(m, k, seed, 0)
+    wg_np, wu_np = workloads.weights(n, k, seed, 1), workloads.weights(n, k, seed, 2)
+    qg = gpu_quantize_int4(dev_f16(wg_np), group)
+    qu = gpu_quantize_int4(dev_f16(wu_np), group)
+    yg = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    yu = torch.empty_like(yg)
+    wq.wq_linear_w4a16_gate_up(dev_f16(x_np), qg, qu, yg, yu if act == 0 else None, act=act)
+    torch.cuda.synchronize()
+    g = oracle_linear(x_np, wg_np, "f16", group=group)
+    u = oracle_linear(x_np, wu_np, "f16", group=group)
+    if act == 0:
+        check_close(to_np(yg), g, "f32")
+        check_close(to_np(yu), u, "f32")
+    else:
+        check_close(to_np(yg), linear.silu_gated(g, u), "f32")
 
 
 def test_linear_prefill_full_shape_sampled():

@@ -147,3 +147,53 @@ def packed_bytes(n, k, group=128):
     """HBM bytes of one packed layer: codes + fp16 scales + 4-bit zeros."""
     g = k // group
     return n * k // 2 + n * g * 2 + n * ((g + 1) // 2)
+
+
+# ------------------------------------------------------------------ act-order
+#
+# Act-order (GPTQ's desc_act): the input channels are quantized in an order
+# set by activation importance, so the groups of 128 run along that order,
+# not along k; inference then has to reorder ([P1] section 3.2; [P4]
+# section 3.2; [P5] section 3.4 on the slower inference).  Reading taken:
+# the order is a permutation ``perm`` of 0..K-1 given by the caller
+# (choosing it needs calibration data, which is out of scope); position j of
+# the quantization order is input channel perm[j]; the group of channel c is
+# g_idx[c] = (position of c in perm) // group.
+
+def g_idx(perm, group=128):
+    """Group of every original input channel: g_idx[perm[j]] = j // group."""
+    perm = np.asarray(perm, dtype=np.int64)
+    g = np.empty(perm.size, dtype=np.int64)
+    g[perm] = np.arange(perm.size) // group
+    return g
+
+
+def dequantize_act_order(w16, perm, group=128, out_dtype="f16"):
+    """The act-order dequantized weight in the ORIGINAL channel order.
+
+    The group statistics are taken over the channels each group holds
+    (those c with g_idx[c] == g), then every weight is encoded with its own
+    group's scale and zero point and dequantized:
+    w_hat[n][c] = round16((q[n][c] - z[n][g_idx[c]]) * s16[n][g_idx[c]]).
+    """
+    w = f32(w16)
+    n, k = w.shape
+    gi = g_idx(perm, group)
+    G = k // group
+    out = np.empty((n, k), dtype=np.float32)
+    for g in range(G):
+        cols = np.nonzero(gi == g)[0]
+        s16, z = group_params(np.asarray(w16)[:, cols], group=cols.size)
+        s = s16.astype(np.float32)                    # [n][1]
+        q = np.clip(rne(w[:, cols] / s) + z, 0, QMAX)
+        out[:, cols] = round_to((q - z).astype(np.float32) * s, out_dtype)
+    return out
+
+
+def quantize_act_order(w16, perm, group=128):
+    """Act-order storage: the weight with its columns in quantization order,
+    W[:, perm], quantized with contiguous groups -- ``(qweight, scales,
+    zeros)`` exactly as :func:`quantize` packs them.  Dequantizing it and
+    scattering the columns back (column j to channel perm[j]) gives
+    :func:`dequantize_act_order`; x[:, perm] times it gives the same y."""
+    return quantize(np.asarray(w16)[:, np.asarray(perm)], group)

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import int4
+import workloads
 from golden_util import load
 
 
@@ -204,3 +205,43 @@ def test_memory_figures_from_the_pages():
     per_param = scale_bytes / (n * k)
     q = float(gold["params_qwen2_1_5b"]) * per_param / 1e9
     assert q == pytest.approx(float(gold["scale_gb_qwen2_1_5b"]), rel=0.03)
+
+
+def _perm(k, seed):
+    """A synthetic act-order: channels by decreasing seeded importance."""
+    return np.argsort(-np.random.default_rng(seed).random(k), kind="stable")
+
+
+def test_act_order_identity_is_plain_quantization():
+    w = workloads.weights(24, 512, 4, 1)
+    ident = np.arange(512)
+    plain = int4.dequantize(*int4.quantize(w), 512)
+    np.testing.assert_array_equal(int4.dequantize_act_order(w, ident), plain)
+    for a, b in zip(int4.quantize_act_order(w, ident), int4.quantize(w)):
+        assert np.array_equal(a, b)
+
+
+def test_act_order_two_formulations_agree():
+    """Storage in quantization order (contiguous groups of W[:, perm]) and
+    the original-order g_idx definition give the same dequantized weights
+    channel by channel."""
+    n, k = 16, 768
+    w = workloads.weights(n, k, 5, 1)
+    perm = _perm(k, 9)
+    stored = int4.dequantize(*int4.quantize_act_order(w, perm), k)
+    back = np.empty_like(stored)
+    back[:, perm] = stored
+    np.testing.assert_array_equal(back, int4.dequantize_act_order(w, perm))
+    # and it is not the plain quantization
+    assert not np.array_equal(back, int4.dequantize(*int4.quantize(w), k))
+
+
+def test_act_order_group_membership_brute_force():
+    """Tiny case: the group of each channel found by scanning perm."""
+    k, group = 256, 128
+    perm = _perm(k, 3)
+    gi = int4.g_idx(perm, group)
+    for c in range(k):
+        pos = [j for j in range(k) if perm[j] == c][0]
+        assert gi[c] == pos // group
+    assert np.bincount(gi).tolist() == [group] * (k // group)

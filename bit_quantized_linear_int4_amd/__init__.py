@@ -19,6 +19,7 @@ __all__ = [
     "FMT_INT4_ASYM", "FMT_NF4", "FMT_INT8_SYM_ROW",
     "wq_quantize_groupwise", "wq_pack_nf4", "wq_nf4_codebook", "wq_pack_fp4", "wq_fp4_codebook",
     "wq_linear_w4a16_workspace", "wq_linear_w4a16", "wq_linear_w4a16_gate_up",
+    "wq_permute_columns",
     "wq_int8_prepare_activations", "wq_linear_int8_decomp_workspace",
     "wq_linear_int8_decomp", "wq_dequantize", "wq_status_string",
     "alloc_int4", "alloc_nf4", "alloc_fp4", "alloc_int8", "library_path", "FMT_FP4",
@@ -47,6 +48,7 @@ class _Weight(ctypes.Structure):
         ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
         ("zeros", ctypes.c_void_p), ("scales2", ctypes.c_void_p),
         ("group2", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("perm", ctypes.c_void_p),
     ]
 
 
@@ -84,6 +86,7 @@ def _load():
         "wq_linear_int8_decomp": (c_i32, [c_vp, c_i64, wp, c_f, c_vp, c_i32, c_vp,
                                           ctypes.c_size_t, c_vp, c_vp, c_vp]),
         "wq_dequantize": (c_i32, [wp, c_vp, c_i32, c_vp]),
+        "wq_permute_columns": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_vp, c_vp]),
         "wq_status_string": (ctypes.c_char_p, [c_i32]),
     }
     for name, (res, args) in sig.items():
@@ -127,10 +130,12 @@ def _stream(stream, t):
 class QuantizedWeight:
     """Device tensors of one quantized weight plus its wq_weight descriptor."""
 
-    def __init__(self, fmt, n, k, group, codes, scales, zeros=None, scales2=None, group2=0):
+    def __init__(self, fmt, n, k, group, codes, scales, zeros=None, scales2=None, group2=0,
+                 perm=None):
         self.fmt, self.n, self.k, self.group = fmt, int(n), int(k), int(group)
         self.codes, self.scales, self.zeros, self.scales2 = codes, scales, zeros, scales2
         self.group2 = int(group2)
+        self.perm = perm          # INT4 act-order: device int32 [k], or None
 
     def descriptor(self):
         d = _Weight()
@@ -141,6 +146,7 @@ class QuantizedWeight:
         d.scales2 = self.scales2.data_ptr() if self.scales2 is not None else None
         d.group2 = self.group2
         d.reserved = 0
+        d.perm = self.perm.data_ptr() if self.perm is not None else None
         return d
 
     def nbytes(self):
@@ -150,7 +156,8 @@ class QuantizedWeight:
     def clone(self):
         c = lambda t: None if t is None else t.clone()
         return QuantizedWeight(self.fmt, self.n, self.k, self.group, c(self.codes),
-                               c(self.scales), c(self.zeros), c(self.scales2), self.group2)
+                               c(self.scales), c(self.zeros), c(self.scales2), self.group2,
+                               c(self.perm))
 
 
 def alloc_int4(n, k, group=128, device="cuda"):
@@ -261,6 +268,13 @@ def wq_linear_int8_decomp(x, weight, threshold, y, workspace, outlier_count=None
                                        _ptr(y), _dt(y), _ptr(workspace), ws_bytes,
                                        _ptr(outlier_count), _ptr(acc_out), _stream(stream, x))
     _check(st, "wq_linear_int8_decomp")
+
+
+def wq_permute_columns(src, perm, dst, stream=None):
+    rows, k = src.shape
+    st = _load().wq_permute_columns(_ptr(src), _dt(src), rows, k, _ptr(perm), _ptr(dst),
+                                    _stream(stream, src))
+    _check(st, "wq_permute_columns")
 
 
 def wq_dequantize(weight, out, stream=None):

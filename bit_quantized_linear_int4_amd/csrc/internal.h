@@ -89,6 +89,10 @@ hipError_t launch_int8_gemm(const uint16_t* x, int64_t m, const wq_weight* w,
                             const int32_t* count, void* y, int ydt, int32_t* acc_out,
                             hipStream_t s);
 
+// dst[r][j] = src[r][perm[j]] for a 16-bit [rows][k] matrix (k % 8 == 0)
+hipError_t launch_permute_cols(const uint16_t* src, int64_t rows, int64_t k,
+                               const int32_t* perm, uint16_t* dst, hipStream_t s);
+
 hipError_t launch_dequantize(const wq_weight* w, const float* levels16, void* out, int odt,
                              hipStream_t s);
 

@@ -33,6 +33,10 @@ wq_status check_weight(const wq_weight* w, bool linear_w4) {
   if (w == nullptr || w->codes == nullptr || w->scales == nullptr) return WQ_ERR_NULL;
   if (!sizes_ok(w->n, w->k)) return WQ_ERR_SHAPE;
   if (!aligned(w->codes, 16)) return WQ_ERR_ALIGN;
+  if (w->perm != nullptr) {
+    if (w->fmt != WQ_FMT_INT4_ASYM) return WQ_ERR_UNSUPPORTED;   // act-order is INT4 only
+    if (!aligned(w->perm, 4)) return WQ_ERR_ALIGN;
+  }
   switch (w->fmt) {
     case WQ_FMT_INT4_ASYM:
       if (w->zeros == nullptr) return WQ_ERR_NULL;
@@ -56,6 +60,15 @@ wq_status check_weight(const wq_weight* w, bool linear_w4) {
     default:
       return WQ_ERR_UNSUPPORTED;
   }
+}
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Workspace of wq_linear_w4a16: the schedule's partial sums, then (act-order)
+// the gathered activations.
+size_t linear_ws_bytes(size_t plan_ws, int64_t m, const wq_weight* w) {
+  if (w->perm == nullptr) return plan_ws;
+  return round256(plan_ws) + round256((size_t)m * (size_t)w->k * 2);
 }
 
 // FP4 weights run the NF4 kernels with the FP4 level table.
@@ -163,7 +176,7 @@ wq_status wq_pack_fp4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t 
 size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w) {
   if (m < 1 || m >= kMaxDim || check_weight(w, true) != WQ_OK) return 0;
   const wq_weight kv = kernel_view(w);
-  return plan_w4a16(m, &kv).ws;
+  return linear_ws_bytes(plan_w4a16(m, &kv).ws, m, w);
 }
 
 wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight* w, void* y,
@@ -178,12 +191,21 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight
   if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;
   const wq_weight kv = kernel_view(w);
   const W4Plan plan = plan_w4a16(m, &kv);
-  if (plan.ws > 0) {
-    if (workspace == nullptr || ws_bytes < plan.ws) return WQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return WQ_ERR_ALIGN;
+  const size_t need = linear_ws_bytes(plan.ws, m, w);
+  if (need > 0) {
+    if (workspace == nullptr || ws_bytes < need) return WQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
   }
-  return hip_status(launch_w4a16(x, xdt, m, &kv, levels_for(w), y, ydt, workspace, plan,
-                                 static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w->perm != nullptr) {
+    // act-order: x[:, perm] into the workspace, then the plain linear on it
+    void* xp = static_cast<char*>(workspace) + round256(plan.ws);
+    const hipError_t e = launch_permute_cols(static_cast<const uint16_t*>(x), m, w->k, w->perm,
+                                             static_cast<uint16_t*>(xp), s);
+    if (e != hipSuccess) return WQ_ERR_HIP;
+    x = xp;
+  }
+  return hip_status(launch_w4a16(x, xdt, m, &kv, levels_for(w), y, ydt, workspace, plan, s));
 }
 
 wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
@@ -197,6 +219,7 @@ wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
   st = check_weight(w_up, true);
   if (st != WQ_OK) return st;
   if (w_gate->fmt != WQ_FMT_INT4_ASYM || w_up->fmt != WQ_FMT_INT4_ASYM) return WQ_ERR_UNSUPPORTED;
+  if (w_gate->perm != nullptr || w_up->perm != nullptr) return WQ_ERR_UNSUPPORTED;
   if (!is16(xdt) || !is_out(ydt)) return WQ_ERR_UNSUPPORTED;
   if (w_gate->n != w_up->n || w_gate->k != w_up->k || w_gate->group != w_up->group ||
       w_gate->k % 128 != 0)
@@ -270,6 +293,18 @@ wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w, fl
     if (e != hipSuccess) return WQ_ERR_HIP;
   }
   return WQ_OK;
+}
+
+wq_status wq_permute_columns(const void* src, int32_t dt, int64_t rows, int64_t k,
+                             const int32_t* perm, void* dst, void* stream) {
+  if (src == nullptr || perm == nullptr || dst == nullptr) return WQ_ERR_NULL;
+  if (!is16(dt)) return WQ_ERR_UNSUPPORTED;
+  if (src == dst) return WQ_ERR_UNSUPPORTED;                 // not in place
+  if (!sizes_ok(rows, k) || k % 8 != 0) return WQ_ERR_SHAPE;
+  if (!aligned(src, 2) || !aligned(dst, 16) || !aligned(perm, 4)) return WQ_ERR_ALIGN;
+  return hip_status(launch_permute_cols(static_cast<const uint16_t*>(src), rows, k, perm,
+                                        static_cast<uint16_t*>(dst),
+                                        static_cast<hipStream_t>(stream)));
 }
 
 wq_status wq_dequantize(const wq_weight* w, void* out, int32_t odt, void* stream) {

@@ -87,6 +87,12 @@ typedef enum {
  *    scales2 fp32 [ceil(n*k/group / group2)] second-level scales, or NULL.
  *    group   NF4 block size (64); group2 the double-quant block (256).
  *  fmt = WQ_FMT_FP4: the NF4 layout with E2M1 codes (see wq_pack_fp4).
+ *  perm (INT4 only, optional): act-order.  The input channels were
+ *    quantized in the order perm[0], perm[1], ... ([P1] 3.2, [P4] 3.2), so
+ *    the groups run along that order: codes, scales and zeros hold the
+ *    columns in that order (column j is input channel perm[j]; quantize
+ *    W[:, perm], made by wq_permute_columns).  wq_linear_w4a16 then gathers
+ *    x[:, perm] into its workspace before the multiply.  NULL: plain order.
  *  fmt = WQ_FMT_INT8_SYM_ROW:
  *    codes   int8 [n][k], 16-byte aligned; scales fp32 [n]; group = k.
  */
@@ -100,6 +106,7 @@ typedef struct {
   const float* scales2;   /* NF4 double quantization only, else NULL          */
   int32_t group2;
   int32_t reserved;
+  const int32_t* perm;    /* INT4 act-order: device int32 [k], else NULL      */
 } wq_weight;
 
 /*
@@ -186,7 +193,8 @@ wq_status wq_nf4_codebook(float* out);
 
 /*
  * Scratch bytes wq_linear_w4a16 needs for this (m, weight) pair: 0 when the
- * chosen schedule needs none.  Returns 0 for invalid arguments as well (the
+ * chosen schedule needs none; an act-order weight needs m * k * 2 bytes
+ * (rounded up to 256) for the gathered activations.  Returns 0 for invalid arguments as well (the
  * call itself then reports the error).
  */
 size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w);
@@ -207,7 +215,9 @@ size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w);
  * (group 128, 64 or 32: the group-size knob of [P5] 2.2 and [P1] 3.2), NF4
  * or FP4 (block 64).  y: ydt in {F16, BF16, F32}, [m][n].
  * workspace: at least wq_linear_w4a16_workspace(m, w) bytes, 256-byte
- * aligned (may be NULL when that is 0).  m >= 1; k % 128 == 0.
+ * aligned (may be NULL when that is 0).  m >= 1; k % 128 == 0.  With
+ * w->perm set (INT4 act-order) the activations are gathered into the
+ * workspace first; NF4/FP4 with perm give WQ_ERR_UNSUPPORTED.
  */
 wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m,
                           const wq_weight* w, void* y, int32_t ydt,
@@ -229,7 +239,8 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m,
  * INT4_ASYM (group 128, 64 or 32) with equal n and k.  y_gate, y_up: ydt in
  * {F16, BF16, F32}, [m][n] each (y_up may be NULL when act = 1).
  * Errors: WQ_ERR_SHAPE when n, k or the group size differ; WQ_ERR_UNSUPPORTED for NF4,
- * act outside {0, 1}, or act = 1 with m > 16.  No workspace.
+ * act-order weights, act outside {0, 1}, or act = 1 with m > 16.  No
+ * workspace.
  */
 wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
                                   const wq_weight* w_gate, const wq_weight* w_up,
@@ -274,7 +285,18 @@ wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w,
                                 void* stream);
 
 /*
- * Dequantize a whole weight into 16-bit values (a test and debugging hook):
+ * Column gather (act-order reordering, [P1] 3.2, [P4] 3.2):
+ *   dst[r][j] = src[r][perm[j]],  r < rows, j < k.
+ * src, dst: dt in {F16, BF16} [rows][k], distinct buffers, dst 16-byte
+ * aligned; perm: device int32 [k], a permutation of 0..k-1 (entries outside
+ * [0, k) are clamped: wrong values, no out-of-bounds access); k % 8 == 0.
+ */
+wq_status wq_permute_columns(const void* src, int32_t dt, int64_t rows, int64_t k,
+                             const int32_t* perm, void* dst, void* stream);
+
+/*
+ * Dequantize a whole weight into 16-bit values (a test and debugging hook;
+ * an act-order weight comes out in its stored column order):
  * INT4: fp(q - z) * s rounded to odt; NF4, FP4: L[code] * a_hat rounded to odt;
  * INT8: fp32(q) * s rounded to odt.  out: odt in {F16, BF16} [n][k].
  */

@@ -116,12 +116,44 @@ def test_pack_nf4_argument_errors(entry):
 
 
 def _weight(fmt=wq.FMT_INT4_ASYM, n=64, k=256, group=128, codes=A16, scales=A16, zeros=A16,
-            scales2=None, group2=0):
+            scales2=None, group2=0, perm=None):
     d = wq._Weight()
     d.fmt, d.group, d.n, d.k = fmt, group, n, k
     d.codes, d.scales, d.zeros, d.scales2 = codes, scales, zeros, scales2
+    d.perm = perm
     d.group2 = group2
     return d
+
+
+def test_act_order_argument_errors():
+    f = _lib().wq_linear_w4a16
+    ws_q = _lib().wq_linear_w4a16_workspace
+
+    def call(w, ws=None, wsb=0):
+        return f(A16, wq.F16, 16, ctypes.byref(w), A16, wq.F32, ws, wsb, None)
+
+    ao = _weight(n=64, k=256, perm=A16)
+    # the gathered activations: 16 x 256 x 2 bytes, rounded to 256
+    assert ws_q(16, ctypes.byref(ao)) == 8192
+    assert ws_q(16, ctypes.byref(_weight())) == 0
+    assert call(ao) == WS                                # no workspace for the gather
+    assert call(ao, A16, 4096) == WS                     # too small
+    assert call(ao, A16 + 16, 8192) == ALIGN             # 256-byte workspace alignment
+    assert call(_weight(perm=A16 + 2)) == ALIGN
+    nf4w = _weight(fmt=wq.FMT_NF4, group=64, zeros=None, perm=A16)
+    assert call(nf4w) == UNSUP                           # act-order is INT4 only
+    g = _lib().wq_linear_w4a16_gate_up
+    assert g(A16, wq.F16, 1, ctypes.byref(ao), ctypes.byref(_weight()), 0, A16, A16, wq.F32,
+             None) == UNSUP
+    p = _lib().wq_permute_columns
+    assert p(None, wq.F16, 4, 64, A16, A16 + 4096, None) == NULL
+    assert p(A16, wq.F16, 4, 64, None, A16 + 4096, None) == NULL
+    assert p(A16, wq.F32, 4, 64, A16, A16 + 4096, None) == UNSUP
+    assert p(A16, wq.F16, 4, 64, A16, A16, None) == UNSUP   # not in place
+    assert p(A16, wq.F16, 4, 60, A16, A16 + 4096, None) == SHAPE
+    assert p(A16, wq.F16, 0, 64, A16, A16 + 4096, None) == SHAPE
+    assert p(A16, wq.F16, 4, 64, A16, A16 + 4104, None) == ALIGN
+    assert p(A16, wq.F16, 4, 64, A16 + 2, A16 + 4096, None) == ALIGN
 
 
 def test_gate_up_argument_errors():

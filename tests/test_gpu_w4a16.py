@@ -263,6 +263,50 @@ def test_gate_up_group_sizes(m, n, k, group, act):
         check_close(to_np(yg), linear.silu_gated(g, u), "f32")
 
 
+def _act_order_perm(k, seed):
+    """A synthetic act-order: channels by decreasing seeded importance."""
+    return np.argsort(-np.random.default_rng(seed).random(k), kind="stable").astype(np.int32)
+
+
+@pytest.mark.parametrize("rows,k,dt", [(37, 1152, "f16"), (5, 4096, "bf16"), (2048, 4096, "f16")])
+def test_permute_columns_bitexact(rows, k, dt):
+    say(f"permute_columns rows={rows} k={k} dt={dt}")
+    src = workloads.weights(rows, k, rows + k, 1, dtype=dt)
+    perm = _act_order_perm(k, rows)
+    out = torch.empty((rows, k), dtype=torch_dtype(dt), device="cuda")
+    wq.wq_permute_columns(dev(src, dt), torch.from_numpy(perm).cuda(), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), host16(src, dt)[:, perm].astype(np.float32))
+
+
+@pytest.mark.parametrize("m,n,k,group", [
+    (1, 300, 1152, 128), (16, 4096, 4096, 128), (16, 1000, 2048, 64), (300, 520, 4096, 128),
+])
+def test_act_order_linear_parity(m, n, k, group):
+    """Act-order weights (columns stored in quantization order) against the
+    oracle's original-order g_idx definition; the stored codes, scales and
+    zeros bit for bit against the oracle's act-order packing."""
+    say(f"act_order m={m} n={n} k={k} group={group}")
+    seed = 800 + m + n
+    x, _ = workloads.activations(m, k, seed, 0, outliers=(min(6, k // 128), 20.0, 80.0))
+    w = workloads.weights(n, k, seed, 1)
+    perm = _act_order_perm(k, seed)
+    perm_d = torch.from_numpy(perm).cuda()
+    w_perm = torch.empty((n, k), dtype=torch.float16, device="cuda")
+    wq.wq_permute_columns(dev_f16(w), perm_d, w_perm)
+    qw = gpu_quantize_int4(w_perm, group)
+    qw.perm = perm_d
+    torch.cuda.synchronize()
+    rq, rs, rz = int4.quantize_act_order(w, perm, group)
+    assert np.array_equal(qw.codes.cpu().numpy().view(np.uint32), rq)
+    assert np.array_equal(qw.scales.cpu().numpy().view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(qw.zeros.cpu().numpy(), rz)
+    y, _ = run_linear(x, w, "f16", "f32", qw=qw)
+    ref = linear.reference(host16(x, "f16"), int4.dequantize_act_order(w, perm, group))
+    rel = check_close(y, ref, "f32")
+    say(f"  max-rel {rel:.2e}")
+
+
 def test_linear_prefill_full_shape_sampled():
     """The prefill layer at full size (M = 2048, up-projection 11008 x 4096):
     every output column of 64 sampled token rows against the oracle."""

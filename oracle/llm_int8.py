@@ -34,7 +34,7 @@ Readings taken where the pages are silent:
 
 import numpy as np
 
-from .numerics import f32, rne, round_f16
+from .numerics import f32, rne, round_f16, round_to
 
 QMAX = 127
 
@@ -108,3 +108,31 @@ def linear(x16, qw, sw, threshold=6.0):
         wo = dequant_weight_f16(qw[:, outl], sw).astype(np.float64)
         y = y + xo @ wo.T
     return y, outl, qx, sx, acc
+
+
+# --------------------------------------------------------- SmoothQuant W8A8
+#
+# W8A8 with smoothing ([P1] section 5): Wx = (W diag(s)^-1)(diag(s) x) holds
+# exactly, so part of the activations' range is moved into the weights;
+# alpha (about 0.5) sets how much; the scaling is folded into the weights
+# offline, which are then stored as INT8 and multiplied by INT8 activations
+# (the decomposition above with no outlier columns, threshold = +inf).
+# Reading taken (the pages print no formula for s): per input channel c,
+# s_c = max|X_c|^alpha / max|W_c|^(1 - alpha) from calibration maxima
+# (given by the caller; here synthetic), activations divided by s and weight
+# columns multiplied by s, each product in fp32 and rounded once to the
+# 16-bit type.
+
+def smooth_factors(x_absmax, w_absmax, alpha=0.5):
+    """s_c = max|X_c|^alpha / max|W_c|^(1 - alpha) in fp64, returned as fp32
+    (channels with a zero maximum get s = 1)."""
+    ax = np.asarray(x_absmax, np.float64)
+    aw = np.asarray(w_absmax, np.float64)
+    s = np.where((ax > 0) & (aw > 0), ax ** alpha / np.where(aw > 0, aw, 1.0) ** (1.0 - alpha), 1.0)
+    return s.astype(np.float32)
+
+
+def scale_columns(a16, scale, out_dtype="f16"):
+    """round16(a[r][c] * scale[c]): fp32 product, one rounding."""
+    prod = f32(a16) * np.asarray(scale, np.float32)[None, :]
+    return round_to(prod, out_dtype)

@@ -121,3 +121,35 @@ def test_decomposition_close_to_float_product():
     y_all, o2, *_ = llm_int8.linear(d["x"], qw, sw, threshold=np.inf)
     rel_all = np.abs(y_all - ref).max() / np.abs(ref).max()
     assert o2.size == 0 and rel_all > 2 * rel
+
+
+def test_smoothing_is_an_exact_migration():
+    """(x / s) . (W * s)^T equals x . W^T before any rounding ([P1] 5.1)."""
+    d = workloads.int8_70b(m=8, n=16, k=256, n_outliers=4)
+    x, w = d["x"].astype(np.float64), d["w"].astype(np.float64)
+    s = llm_int8.smooth_factors(np.abs(x).max(axis=0), np.abs(w).max(axis=0)).astype(np.float64)
+    np.testing.assert_allclose((x / s) @ (w * s).T, x @ w.T, rtol=1e-12, atol=1e-12)
+
+
+def test_smoothing_balances_the_ranges_at_alpha_half():
+    """With alpha = 1/2 every channel's activation and weight maxima become
+    equal (both sqrt(max|X| max|W|)); alpha = 0 scales every weight column
+    to maximum 1, alpha = 1 every activation column."""
+    rng = np.random.default_rng(1)
+    ax, aw = rng.uniform(0.1, 80, 64), rng.uniform(0.001, 0.1, 64)
+    s = llm_int8.smooth_factors(ax, aw, 0.5).astype(np.float64)
+    np.testing.assert_allclose(ax / s, aw * s, rtol=1e-6)
+    np.testing.assert_allclose(ax / s, np.sqrt(ax * aw), rtol=1e-6)
+    s0 = llm_int8.smooth_factors(ax, aw, 0.0).astype(np.float64)
+    np.testing.assert_allclose(aw * s0, np.ones(64), rtol=1e-6)
+    s1 = llm_int8.smooth_factors(ax, aw, 1.0).astype(np.float64)
+    np.testing.assert_allclose(ax / s1, np.ones(64), rtol=1e-6)
+    assert llm_int8.smooth_factors([0.0, 2.0], [1.0, 0.0]).tolist() == [1.0, 1.0]
+
+
+def test_scale_columns_rounds_once():
+    a = np.array([[1.0, 3.0, -2.5, 1e-3]], np.float16)
+    sc = np.array([0.5, 1.0 / 3.0, 4.0, 7.0], np.float32)
+    got = llm_int8.scale_columns(a, sc, "f16")
+    ref = (a.astype(np.float32) * sc).astype(np.float16).astype(np.float32)
+    np.testing.assert_array_equal(got, ref)

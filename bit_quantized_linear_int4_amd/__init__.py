@@ -19,7 +19,7 @@ __all__ = [
     "FMT_INT4_ASYM", "FMT_NF4", "FMT_INT8_SYM_ROW",
     "wq_quantize_groupwise", "wq_pack_nf4", "wq_nf4_codebook", "wq_pack_fp4", "wq_fp4_codebook",
     "wq_linear_w4a16_workspace", "wq_linear_w4a16", "wq_linear_w4a16_gate_up",
-    "wq_permute_columns",
+    "wq_permute_columns", "wq_scale_columns",
     "wq_int8_prepare_activations", "wq_linear_int8_decomp_workspace",
     "wq_linear_int8_decomp", "wq_dequantize", "wq_status_string",
     "alloc_int4", "alloc_nf4", "alloc_fp4", "alloc_int8", "library_path", "FMT_FP4",
@@ -87,6 +87,7 @@ def _load():
                                           ctypes.c_size_t, c_vp, c_vp, c_vp]),
         "wq_dequantize": (c_i32, [wp, c_vp, c_i32, c_vp]),
         "wq_permute_columns": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_vp, c_vp]),
+        "wq_scale_columns": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_vp, c_vp]),
         "wq_status_string": (ctypes.c_char_p, [c_i32]),
     }
     for name, (res, args) in sig.items():
@@ -275,6 +276,13 @@ def wq_permute_columns(src, perm, dst, stream=None):
     st = _load().wq_permute_columns(_ptr(src), _dt(src), rows, k, _ptr(perm), _ptr(dst),
                                     _stream(stream, src))
     _check(st, "wq_permute_columns")
+
+
+def wq_scale_columns(src, scale, dst, stream=None):
+    rows, k = src.shape
+    st = _load().wq_scale_columns(_ptr(src), _dt(src), rows, k, _ptr(scale), _ptr(dst),
+                                  _stream(stream, src))
+    _check(st, "wq_scale_columns")
 
 
 def wq_dequantize(weight, out, stream=None):

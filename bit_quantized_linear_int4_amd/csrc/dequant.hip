@@ -42,12 +42,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(wq_weight w, Levels lv,
     else
       ah = static_cast<const float*>(w.scales)[blk];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = lv.v[(word >> (4 * i)) & 15u] * ah;
+    for (int i = 0; i < 8; ++i) v[i] = as_f32(lv.v[(word >> (4 * i)) & 15u] * ah);
   } else {
     const int8_t* q = static_cast<const int8_t*>(w.codes) + e0;
     const float s = static_cast<const float*>(w.scales)[r];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)q[i] * s;
+    for (int i = 0; i < 8; ++i) v[i] = as_f32((float)q[i] * s);
   }
   uint4_t o;
 #pragma unroll

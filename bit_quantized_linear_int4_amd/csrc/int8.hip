@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void int8_gemm_kernel(Int8GemmArgs a) {
       uint16_t v = 0;
       if (c0 + j < cnt && n0 + r < a.n) {
         const float wq = (float)a.qw[(int64_t)(n0 + r) * a.k + a.idx[c0 + j]];
-        v = f32_to_f16_bits(wq * a.sw[n0 + r]);
+        v = f32_to_f16_bits(as_f32(wq * a.sw[n0 + r]));
       }
       Wo[r * 40 + j] = v;
     }

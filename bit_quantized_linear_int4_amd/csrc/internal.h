@@ -28,6 +28,16 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
+// An fp32 value held in a register as is.  Narrowing a product to 16 bits
+// right after it lets the compiler fuse both into one mixed-precision
+// multiply (v_fma_mixlo_f16) that rounds the exact product once; where the
+// definition is "the fp32 product, then a 16-bit rounding" and the product
+// is not exact in fp32, pass it through here first.  The empty asm emits
+// nothing.
+__device__ __forceinline__ float as_f32(float v) {
+  asm("" : "+v"(v));
+  return v;
+}
 // fp32 -> fp16, round to nearest even (v_cvt_f16_f32).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   _Float16 h = (_Float16)v;
@@ -92,6 +102,10 @@ hipError_t launch_int8_gemm(const uint16_t* x, int64_t m, const wq_weight* w,
 // dst[r][j] = src[r][perm[j]] for a 16-bit [rows][k] matrix (k % 8 == 0)
 hipError_t launch_permute_cols(const uint16_t* src, int64_t rows, int64_t k,
                                const int32_t* perm, uint16_t* dst, hipStream_t s);
+
+// dst[r][c] = round16(src[r][c] * scale[c]) (in place allowed; k % 8 == 0)
+hipError_t launch_scale_cols(const uint16_t* src, int dt, int64_t rows, int64_t k,
+                             const float* scale, uint16_t* dst, hipStream_t s);
 
 hipError_t launch_dequantize(const wq_weight* w, const float* levels16, void* out, int odt,
                              hipStream_t s);

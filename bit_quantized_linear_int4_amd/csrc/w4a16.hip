@@ -159,8 +159,8 @@ __device__ __forceinline__ uint4_t dequant_nf4_word(uint32_t w, const float* lut
   uint4_t b;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float v0 = lut[(w >> (8 * e)) & 15u] * ah;
-    const float v1 = lut[(w >> (8 * e + 4)) & 15u] * ah;
+    const float v0 = as_f32(lut[(w >> (8 * e)) & 15u] * ah);
+    const float v1 = as_f32(lut[(w >> (8 * e + 4)) & 15u] * ah);
     b[e] = (uint32_t)f32_to_x<XDT>(v0) | ((uint32_t)f32_to_x<XDT>(v1) << 16);
   }
   return b;
@@ -630,8 +630,8 @@ __device__ __forceinline__ void dequant32(const GemmArgs& a, const float* lut, i
       const uint32_t w = wv[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v0 = lut[(w >> (8 * e)) & 15u] * ah;
-        const float v1 = lut[(w >> (8 * e + 4)) & 15u] * ah;
+        const float v0 = as_f32(lut[(w >> (8 * e)) & 15u] * ah);
+        const float v1 = as_f32(lut[(w >> (8 * e + 4)) & 15u] * ah);
         out[j * 4 + e] = (uint32_t)f32_to_x<XDT>(v0) | ((uint32_t)f32_to_x<XDT>(v1) << 16);
       }
     }

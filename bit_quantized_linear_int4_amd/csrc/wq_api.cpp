@@ -307,6 +307,17 @@ wq_status wq_permute_columns(const void* src, int32_t dt, int64_t rows, int64_t 
                                         static_cast<hipStream_t>(stream)));
 }
 
+wq_status wq_scale_columns(const void* src, int32_t dt, int64_t rows, int64_t k,
+                           const float* scale, void* dst, void* stream) {
+  if (src == nullptr || scale == nullptr || dst == nullptr) return WQ_ERR_NULL;
+  if (!is16(dt)) return WQ_ERR_UNSUPPORTED;
+  if (!sizes_ok(rows, k) || k % 8 != 0) return WQ_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(scale, 4)) return WQ_ERR_ALIGN;
+  return hip_status(launch_scale_cols(static_cast<const uint16_t*>(src), dt, rows, k, scale,
+                                      static_cast<uint16_t*>(dst),
+                                      static_cast<hipStream_t>(stream)));
+}
+
 wq_status wq_dequantize(const wq_weight* w, void* out, int32_t odt, void* stream) {
   if (out == nullptr) return WQ_ERR_NULL;
   const wq_status st = check_weight(w, false);

@@ -295,6 +295,20 @@ wq_status wq_permute_columns(const void* src, int32_t dt, int64_t rows, int64_t 
                              const int32_t* perm, void* dst, void* stream);
 
 /*
+ * Column scaling for SmoothQuant-style W8A8 ([P1] section 5: the
+ * activation range is moved into the weights by a per-channel s, folded
+ * offline; then the INT8 product runs with no outlier columns, i.e.
+ * wq_linear_int8_decomp with threshold = +inf):
+ *   dst[r][c] = round16(src[r][c] * scale[c])  (fp32 product, one rounding)
+ * Use scale = s on the weights before wq_quantize_groupwise(bits = 8) and
+ * scale = 1/s on the activations.  src, dst: dt in {F16, BF16} [rows][k],
+ * 16-byte aligned, may be the same buffer; scale: device fp32 [k];
+ * k % 8 == 0.
+ */
+wq_status wq_scale_columns(const void* src, int32_t dt, int64_t rows, int64_t k,
+                           const float* scale, void* dst, void* stream);
+
+/*
  * Dequantize a whole weight into 16-bit values (a test and debugging hook;
  * an act-order weight comes out in its stored column order):
  * INT4: fp(q - z) * s rounded to odt; NF4, FP4: L[code] * a_hat rounded to odt;

@@ -156,6 +156,16 @@ def test_act_order_argument_errors():
     assert p(A16, wq.F16, 4, 64, A16 + 2, A16 + 4096, None) == ALIGN
 
 
+def test_scale_columns_argument_errors():
+    f = _lib().wq_scale_columns
+    assert f(None, wq.F16, 4, 64, A16, A16, None) == NULL
+    assert f(A16, wq.F16, 4, 64, None, A16, None) == NULL
+    assert f(A16, wq.F32, 4, 64, A16, A16, None) == UNSUP
+    assert f(A16, wq.F16, 4, 60, A16, A16, None) == SHAPE
+    assert f(A16, wq.F16, 4, 64, A16, A16 + 8, None) == ALIGN
+    assert f(A16, wq.F16, 4, 64, A16 + 2, A16, None) == ALIGN
+
+
 def test_gate_up_argument_errors():
     f = _lib().wq_linear_w4a16_gate_up
 

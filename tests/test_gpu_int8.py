@@ -101,3 +101,52 @@ def test_decomp_70b_shape_sampled():
     assert np.array_equal(acc[:, cols], acc_ref)
     rel = check_close(y[:, cols], y_ref, "f32")
     say(f"  max-rel {rel:.2e}")
+
+
+# ---------------------------------------------------- SmoothQuant-style W8A8
+
+@pytest.mark.parametrize("rows,k,dt", [(37, 1024, "f16"), (8, 512, "bf16")])
+def test_scale_columns_bitexact(rows, k, dt):
+    say(f"scale_columns rows={rows} k={k} dt={dt}")
+    from gpu_util import dev, host16
+    a = workloads.weights(rows, k, rows + k, 1, dtype=dt)
+    sc = np.random.default_rng(rows).uniform(0.05, 20.0, k).astype(np.float32)
+    out = torch.empty((rows, k), dtype=torch_dtype(dt), device="cuda")
+    wq.wq_scale_columns(dev(a, dt), torch.from_numpy(sc).cuda(), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), llm_int8.scale_columns(host16(a, dt), sc, dt))
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 256, 1024), (256, 512, 2048)])
+def test_smoothed_w8a8_parity(m, n, k):
+    """Smoothing (alpha = 0.5, synthetic calibration maxima from the inputs
+    themselves) folded into the weights, activations divided on the GPU,
+    then the INT8 product with no outlier columns: int32 accumulators bit
+    for bit and y against the oracle on the same smoothed inputs.  The
+    smoothing must also cut the error against the unquantized product."""
+    say(f"smoothed_w8a8 m={m} n={n} k={k}")
+    seed = 900 + m + n
+    x, _ = workloads.activations(m, k, seed, 0, outliers=(8, 20.0, 100.0))
+    w = workloads.weights(n, k, seed, 1)
+    s = llm_int8.smooth_factors(np.abs(x.astype(np.float32)).max(axis=0),
+                                np.abs(w.astype(np.float32)).max(axis=0), 0.5)
+    inv = (np.float32(1) / s).astype(np.float32)
+    xs = torch.empty((m, k), dtype=torch.float16, device="cuda")
+    ws_ = torch.empty((n, k), dtype=torch.float16, device="cuda")
+    wq.wq_scale_columns(dev_f16(x), torch.from_numpy(inv).cuda(), xs)
+    wq.wq_scale_columns(dev_f16(w), torch.from_numpy(s).cuda(), ws_)
+    torch.cuda.synchronize()
+    x_ref = llm_int8.scale_columns(x, inv, "f16").astype(np.float16)
+    w_ref = llm_int8.scale_columns(w, s, "f16").astype(np.float16)
+    assert np.array_equal(xs.cpu().numpy(), x_ref) and np.array_equal(ws_.cpu().numpy(), w_ref)
+    y, acc, cnt = run_decomp(x_ref, w_ref, float("inf"), "f32")
+    qw, sw = llm_int8.quantize_rows(w_ref)
+    y_ref, outl, qx, sx, acc_ref = llm_int8.linear(x_ref, qw, sw, float("inf"))
+    assert cnt == 0 and np.array_equal(acc, acc_ref)
+    check_close(y, y_ref, "f32")
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    y_plain, _, _ = run_decomp(x, w, float("inf"), "f32")
+    err_s = np.abs(y - exact).max() / np.abs(exact).max()
+    err_p = np.abs(y_plain - exact).max() / np.abs(exact).max()
+    say(f"  W8A8 error vs fp64: smoothed {err_s:.2e}, plain {err_p:.2e}")
+    assert err_s < err_p

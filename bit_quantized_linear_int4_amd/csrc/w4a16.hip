@@ -766,7 +766,7 @@ constexpr int kGemmWaves = WQ_GEMM_WAVES;   // 4: 128 x 64 per wave; 8: 128 x 32
 constexpr int kGemmScaleBytes = 256 * kGemmMaxGroups * 2;
 constexpr int kGemmZeroBytes = 256 * kGemmMaxGroups / 2;
 
-template <int YDT, int NWG>
+template <int YDT, int NWG, int SUB>   // SUB: INT4 groups per unit of 128 (1, 2, 4)
 __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
   constexpr int NW = NWG, BM = 128, BN = 256;
   constexpr int NF = BN / 16 / NW;               // 16-row code tiles per wave (n)
@@ -801,7 +801,7 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
   const int G = a.G, GS = a.GS;                  // units of 128; groups per row
   const int SCB = (BN * GS * 2 + 1023) / 1024 * 1024;
   const int ZCB = (BN * a.zb + 1023) / 1024 * 1024;
-  const int lq = (kq * a.sub) >> 2;              // this lane's group within a unit
+  const int lq = (kq * SUB) >> 2;                // this lane's group within a unit
 
   // staged scales and zero points of rows n0 .. n0+255 (clamped at the end
   // of the buffers; rows past n are never stored)
@@ -881,7 +881,7 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
     for (int j = 0; j < NF; ++j) {
       const int r = wn * 16 * NF + j * 16 + nl;
       wv[j] = wcur[r * 4 + (kq ^ ((r >> 2) & 3))];
-      const int gq = g * a.sub + lq;
+      const int gq = g * SUB + lq;
       _Float16 sc16;
       __builtin_memcpy(&sc16, scl + (r * GS + gq) * 2, 2);
       const uint32_t zb = zcl[r * a.zb + (gq >> 1)];
@@ -941,7 +941,12 @@ hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
     b.x = a.x + r0 * a.k;
     b.y = static_cast<char*>(a.y) + r0 * a.n * ysz;
     const dim3 grid((unsigned)(ntn * ((b.m + 127) / 128)));
-    gemm_i4_kernel<YDT, NWG><<<grid, NWG * 64, 0, s>>>(b);
+    if (a.sub == 4)
+      gemm_i4_kernel<YDT, NWG, 4><<<grid, NWG * 64, 0, s>>>(b);
+    else if (a.sub == 2)
+      gemm_i4_kernel<YDT, NWG, 2><<<grid, NWG * 64, 0, s>>>(b);
+    else
+      gemm_i4_kernel<YDT, NWG, 1><<<grid, NWG * 64, 0, s>>>(b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

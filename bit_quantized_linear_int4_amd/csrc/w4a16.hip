@@ -28,13 +28,24 @@
 //    about the order of k inside one MFMA).  With bf16 activations the codes
 //    are dequantized exactly, (q - z) * s rounded once to bf16.
 //
-//    NF4 codes are looked up in the 16-level table (LDS), multiplied by the
-//    block's absmax and rounded to the activation type, exactly as the
-//    dequantization defines them.
+//    With INT4 groups of 64 or 32 a unit of 128 holds several groups, which
+//    one MFMA would mix; those weights are dequantized exactly in the B
+//    operand instead ((1024 + q) - (1024 + z), times s, one fp16 rounding).
 //
-//  * gemm (m > 16, prefill).  MFMA-bound: 128x128 output tiles, the weight
-//    tile is dequantized once into LDS in the activation type and both
-//    operands are read from LDS by four waves (64x64 each).
+//    NF4 and FP4 codes are looked up in the 16-level table (LDS), multiplied
+//    by the block's absmax and rounded to the activation type, exactly as
+//    the dequantization defines them.
+//
+//    A gate/up pair sharing x runs as one launch whose workgroups hold the
+//    row tiles of both matrices (the activations are staged once).
+//
+//  * gemm (m > 16, prefill).  MFMA-bound.  gemm_i4_kernel (INT4, fp16
+//    activations, at most 64 groups per row): 128 x 256 workgroup tiles,
+//    8 waves of 128 x 32, activations and codes reach LDS by direct loads
+//    a step or two ahead, every code is dequantized exactly in registers by
+//    the wave that multiplies it, tiles ordered per XCD.  gemm_kernel
+//    (everything else): 128 x 128 tiles, the weight tile dequantized once
+//    into LDS in the activation type, four waves of 64 x 64.
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
@@ -240,8 +251,11 @@ __device__ __forceinline__ void vm_wait_n(int n) { vm_wait_range<0, 63>(n); }
 // The 16-byte chunk c16 of activation row m sits in slot c16 ^ (m & 15) of
 // the row, so the 16 rows an MFMA operand read touches fall in different LDS
 // banks.  LDS is sized at launch (stream_lds_bytes).
+// SG (INT4, fp16 activations): groups of 64 or 32, dequantized exactly in the
+// B operand; a separate instantiation, so the g128 kernels carry none of its
+// registers.
 template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL,
-          bool DUAL>
+          bool DUAL, bool SG>
 __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv, int phases,
                                                          int kslice) {
   // DUAL: TPG counts the tiles of both matrices; tile t < TH is row tile t
@@ -441,7 +455,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
           A[j] = FAST ? perm_x(v) : v;
         }
         if constexpr (FAST) {
-          if (a.sub == 1) {
+          if constexpr (!SG) {
             // one group per unit: the MFMA sums x (1024 + q) over the unit,
             // then s (acc - (1024 + z) X) removes bias and zero point
             float4_t X = {0.f, 0.f, 0.f, 0.f};
@@ -961,9 +975,9 @@ inline int int4_groups(const wq_weight* w) {
 // ---------------------------------------------------------------- launch
 // Streaming decode configurations: NW, TPG, GPP, MP, NBUF.
 template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL,
-          bool DUAL = false>
+          bool DUAL, bool SG>
 hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
-  auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL, DUAL>;
+  auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL, DUAL, SG>;
   const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, DUAL, a.GS, a.zb);
   if (a.m > MP) return hipErrorInvalidValue;   // rows past MP are never staged
   if (lds > 160 * 1024 - 256) return hipErrorInvalidConfiguration;
@@ -990,12 +1004,23 @@ hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& 
 
 template <int XDT, int YDT, int FMT>
 hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
-#define WQ_STR(C, NW, TPG, GPP, MP, NBUF)                                                  \
-  case C:                                                                                  \
-    if constexpr (FMT == WQ_FMT_INT4_ASYM) {                                               \
-      if (p.szl) return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, true>(a, lv, p, s); \
-    }                                                                                      \
-    return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false>(a, lv, p, s);
+#define WQ_STR(C, NW, TPG, GPP, MP, NBUF)                                                     \
+  case C:                                                                                     \
+    if constexpr (FMT == WQ_FMT_INT4_ASYM) {                                                  \
+      if constexpr (XDT == WQ_F16) {                                                          \
+        if (a.sub > 1) {                                                                      \
+          if (p.szl)                                                                          \
+            return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, true, false, true>(  \
+                a, lv, p, s);                                                                 \
+          return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false, false, true>(   \
+              a, lv, p, s);                                                                   \
+        }                                                                                     \
+      }                                                                                       \
+      if (p.szl)                                                                              \
+        return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, true, false, false>(     \
+            a, lv, p, s);                                                                     \
+    }                                                                                         \
+    return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false, false, false>(a, lv, p, s);
   switch (p.cfg) {
     WQ_STR(22, 8, 1, 1, 1, 4)
     WQ_STR(27, 8, 3, 1, 16, 4)
@@ -1019,13 +1044,20 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
 template <int XDT, int YDT>
 hipError_t launch_stream_pair(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
                               hipStream_t s) {
+#define WQ_PAIR_T(NW, TPG, GPP, MP, NBUF, SG)                                                  \
+  if (p.szl)                                                                                  \
+    return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, true, true, SG>( \
+        a, lv, p, s);                                                                         \
+  return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, false, true, SG>(  \
+      a, lv, p, s);
 #define WQ_PAIR(C, NW, TPG, GPP, MP, NBUF)                                                    \
   case C:                                                                                     \
-    if (p.szl)                                                                                \
-      return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, true, true>( \
-          a, lv, p, s);                                                                       \
-    return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, false, true>(  \
-        a, lv, p, s);
+    if constexpr (XDT == WQ_F16) {                                                            \
+      if (a.sub > 1) {                                                                        \
+        WQ_PAIR_T(NW, TPG, GPP, MP, NBUF, true)                                               \
+      }                                                                                       \
+    }                                                                                         \
+    WQ_PAIR_T(NW, TPG, GPP, MP, NBUF, false)
   switch (p.cfg) {
     WQ_PAIR(60, 8, 2, 1, 1, 2)
     WQ_PAIR(61, 8, 2, 1, 4, 2)
@@ -1036,6 +1068,7 @@ hipError_t launch_stream_pair(const SkinnyArgs& a, const Levels& lv, const W4Pla
     default: return hipErrorInvalidConfiguration;
   }
 #undef WQ_PAIR
+#undef WQ_PAIR_T
 }
 
 template <int XDT, int YDT>
@@ -1232,6 +1265,14 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
     const int64_t th = (ntiles + 255) / 256;
     cfg = th >= 4 ? 65 : th == 3 ? 64 : (th == 2 ? 63 : 62);
   }
+#ifdef WQ_TUNE_ENV
+  if (const char* e = getenv("WQ_PAIR")) {
+    int c = -1;
+    if (sscanf(e, "%d", &c) == 1)
+      for (const PCfg& pc : pcfgs)
+        if (pc.id == c && pc.mp >= m) cfg = c;
+  }
+#endif
   for (const PCfg& pc : pcfgs)
     if (pc.id == cfg) {
       p.cfg = pc.id;

@@ -8,10 +8,9 @@
 //   * the two products are summed.
 //
 // Kernels, in launch order:
-//   int8_colflags   per (64-row chunk, column): any |x| > threshold
-//   int8_compact    one workgroup: OR over row chunks -> mask, ascending
-//                   outlier list, count (no host round trip; the count stays
-//                   on the device)
+//   int8_colmask    per column: any |x| > threshold over the rows -> mask
+//   int8_compact    one workgroup: mask -> ascending outlier list, count (no
+//                   host round trip; the count stays on the device)
 //   int8_quant_act  one workgroup per token: absmax over the non-outlier
 //                   columns -> sx, codes (0 in outlier columns)
 //   int8_gemm       256 x BN output tiles: v_mfma_i32_16x16x64_i8 over K, then
@@ -26,23 +25,41 @@
 namespace wq {
 namespace {
 
-constexpr int kRowChunk = 64;
-
-__global__ __launch_bounds__(256) void int8_colflags_kernel(const uint16_t* __restrict__ x,
-                                                            int64_t m, int64_t k, float thr,
-                                                            uint8_t* __restrict__ flags) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= k) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kRowChunk;
-  const int64_t r1 = std::min<int64_t>(m, r0 + kRowChunk);
-  bool any = false;
-  for (int64_t r = r0; r < r1; ++r) any |= fabsf(f16_bits_to_f32(x[r * k + c])) > thr;
-  flags[(int64_t)blockIdx.y * k + c] = any ? 1 : 0;
+// Column mask: workgroup b covers columns 64b .. 64b+63 over every row; a
+// thread reads 8 columns (16 bytes) of rows tid/8, tid/8 + 32, ..., and the
+// 32 row groups' flags are OR-ed in LDS before the mask bytes are written.
+__global__ __launch_bounds__(256) void int8_colmask_kernel(const uint16_t* __restrict__ x,
+                                                           int64_t m, int64_t k, float thr,
+                                                           uint8_t* __restrict__ mask) {
+  __shared__ uint32_t part[32][8];
+  const int t = threadIdx.x, cc = t & 7, rg = t >> 3;
+  const int64_t c0 = (int64_t)blockIdx.x * 64 + cc * 8;
+  uint32_t f = 0;   // bit i: column c0 + i
+  if (c0 < k) {
+#pragma unroll 8
+    for (int64_t r = rg; r < m; r += 32) {
+      const uint4_t v = *reinterpret_cast<const uint4_t*>(x + r * k + c0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint16_t h = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+        if (fabsf(f16_bits_to_f32(h)) > thr) f |= 1u << i;
+      }
+    }
+  }
+  part[rg][cc] = f;
+  __syncthreads();
+  if (t < 64 && (int64_t)blockIdx.x * 64 + t < k) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int g = 0; g < 32; ++g) o |= part[g][t >> 3];
+    mask[(int64_t)blockIdx.x * 64 + t] = (uint8_t)((o >> (t & 7)) & 1u);
+  }
 }
 
-__global__ __launch_bounds__(1024) void int8_compact_kernel(const uint8_t* __restrict__ flags,
-                                                            int64_t k, int chunks,
-                                                            uint8_t* __restrict__ mask,
+// One workgroup: ascending list of the flagged columns and their count (no
+// host round trip; the count stays on the device).
+__global__ __launch_bounds__(1024) void int8_compact_kernel(const uint8_t* __restrict__ mask,
+                                                            int64_t k,
                                                             int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ count) {
   __shared__ int32_t part[1024];
@@ -50,12 +67,7 @@ __global__ __launch_bounds__(1024) void int8_compact_kernel(const uint8_t* __res
   const int64_t per = (k + 1023) / 1024;
   const int64_t c0 = std::min<int64_t>(k, t * per), c1 = std::min<int64_t>(k, c0 + per);
   int32_t n = 0;
-  for (int64_t c = c0; c < c1; ++c) {
-    uint8_t f = 0;
-    for (int j = 0; j < chunks; ++j) f |= flags[(int64_t)j * k + c];
-    mask[c] = f;
-    n += f;
-  }
+  for (int64_t c = c0; c < c1; ++c) n += mask[c];
   part[t] = n;
   __syncthreads();
   // inclusive scan (Hillis-Steele) over 1024 partial counts
@@ -121,12 +133,39 @@ __global__ __launch_bounds__(256) void int8_quant_act_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------- GEMM
-constexpr int IBM = 256, IBK = 128, ILD = IBK + 16;   // bytes per LDS row
+// Workgroup tile 256 (m) x BN = 16*NT (n) with NT = 7 or 8; four waves, wave
+// w owning rows 64w .. 64w+63 of the tile and all BN columns (4 x NT MFMA
+// tiles of 16x16).  K advances 128 bytes per step (two K extents of
+// v_mfma_i32_16x16x64_i8).  Weight rows are in exactly one tile for m <= 256,
+// so the int8 weights stream from HBM once; the activation codes (at most a
+// few MB) are re-read from L2 by every tile.
+//
+//  * Every load lands in registers (global_load_dwordx4): on this GPU a CU
+//    streams about a fifth more through ordinary vector loads than through
+//    direct global->LDS loads, and the compiler then counts every load in its
+//    own waits.
+//  * A wave's activation rows are its own: they are loaded straight into
+//    the MFMA A-operand registers, two steps ahead (RA = 2 register stages).
+//  * The weight slice of a step is shared by the four waves: each thread
+//    loads 4 x 16 bytes of it RB = 4 steps ahead, writes them into one of two
+//    LDS buffers a step before they are multiplied, and one barrier per step
+//    publishes that buffer and proves the other one free.
+//  * 16-byte chunk c of weight row r sits at slot c ^ swz(r) of the row's
+//    eight, so the 16 rows an operand read touches fall in distinct LDS banks
+//    (for both 128- and 256-byte bank rows).
+//  * Epilogue: y = acc * sx[m] * sw[n] in fp32, then the outlier columns in
+//    chunks of 32 through v_mfma_f32_16x16x32_f16 on the fp16 activations and
+//    the int8 weights dequantized to fp16, added into the same registers.
+constexpr int kI8BM = 256, kI8BK = 128;
+constexpr int kI8WS = 128 * kI8BK / 16;      // 16-byte slots per weight buffer (up to 128 rows)
 
-template <int NT>
-struct Int8Tile {
-  static constexpr int BN = NT * 16;
-};
+__device__ __forceinline__ int i8_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima): this wave's
+// LDS writes are done
+__device__ __forceinline__ void lgkm_wait0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
 
 __device__ __forceinline__ int4_t mfma_i8(uint4_t a, uint4_t b, int4_t c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int4_t, a),
@@ -153,35 +192,64 @@ struct Int8GemmArgs {
 template <int NT, int YDT>
 __global__ __launch_bounds__(256) void int8_gemm_kernel(Int8GemmArgs a) {
   constexpr int BN = NT * 16;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[IBM * ILD + BN * ILD];
-  uint8_t* As = smem;
-  uint8_t* Bs = smem + IBM * ILD;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = blockIdx.y * IBM, n0 = blockIdx.x * BN;
+  constexpr int RA = 2, RB = 4;                 // register stages: activations, weights
+  static_assert(NT == 7 || NT == 8, "tile widths 112 and 128");
+  __shared__ uint4_t wsl[2 * kI8WS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15, kc = lane >> 4;
+  const int m0 = (int)blockIdx.y * kI8BM, n0 = (int)blockIdx.x * BN;
+  const int nk = a.k / kI8BK;
 
-  constexpr int AV = IBM * IBK / 16 / 256;   // uint4 per thread for the x tile (8)
-  constexpr int BV = BN * IBK / 16;          // uint4 for the weight tile
-  constexpr int BVT = (BV + 255) / 256;
-  uint4_t ra[AV], rb[BVT];
-  auto load_tile = [&](int k0) {
+  // activation rows of this lane's A operands (rows past m read row m - 1,
+  // never stored): operand (kk, i) = 16 bytes of row wave*64 + i*16 + nl at
+  // byte kk*64 + kc*16 of the step
+  const int8_t* xrow[4];
 #pragma unroll
-    for (int r = 0; r < AV; ++r) {
-      const int i = tid + 256 * r;
-      const int row = i >> 3, col = (i & 7) * 16;
-      if (m0 + row < a.m)
-        ra[r] = *reinterpret_cast<const uint4_t*>(a.qx + (int64_t)(m0 + row) * a.k + k0 + col);
-      else
-        ra[r] = uint4_t{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < 4; ++i)
+    xrow[i] = a.qx + (int64_t)min(m0 + wave * 64 + i * 16 + nl, a.m - 1) * a.k + kc * 16;
+  // weight slots of this thread: slot tid + 256u = row r, chunk c; rows past
+  // BN (NT = 7: waves 2 and 3 for u = 3) are not loaded, rows past n read the
+  // tile's last valid row
+  const int8_t* wsrc[4];
+  int wdst[4];
 #pragma unroll
-    for (int r = 0; r < BVT; ++r) {
-      const int i = tid + 256 * r;
-      if (i < BV) {
-        const int row = i >> 3, col = (i & 7) * 16;
-        const int rg = min(n0 + row, a.n - 1);
-        rb[r] = *reinterpret_cast<const uint4_t*>(a.qw + (int64_t)rg * a.k + k0 + col);
-      }
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int sl = tid + 256 * u, r = sl >> 3, c = sl & 7;
+    wsrc[u] = a.qw + (int64_t)(n0 + min(r, a.n - 1 - n0)) * a.k + c * 16;
+    wdst[u] = r * 8 + (c ^ i8_swz(r));
+  }
+  // K order: every workgroup starts at its own step and wraps around, so at
+  // any moment the workgroups of an XCD (every 8th one) read lines at many
+  // different K offsets, spread over the L2 channels, instead of the same
+  // offset of rows a power of two apart (int32 sums do not depend on the
+  // order)
+  const unsigned bid = blockIdx.x;
+  const int kstart = (int)(((bid >> 3) * 5u + (bid & 7u) * 3u + blockIdx.y * 7u) % (unsigned)nk);
+  auto koff = [&](int g) {
+    int gk = min(g, nk - 1) + kstart;
+    gk -= gk >= nk ? nk : 0;
+    return gk * kI8BK;
+  };
+  auto wload = [&](uint4_t (&wr)[4], int g) {
+    const int off = koff(g);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < 3 || BN == 128 || wave < (BN * 8 - 768) / 64)
+        wr[u] = *reinterpret_cast<const uint4_t*>(wsrc[u] + off);
+  };
+  auto wstore = [&](const uint4_t (&wr)[4], int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < 3 || BN == 128 || wave < (BN * 8 - 768) / 64) wsl[buf * kI8WS + wdst[u]] = wr[u];
+  };
+  auto aload = [&](uint4_t (&ar)[2][4], int g) {
+    const int off = koff(g);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ar[kk][i] = *reinterpret_cast<const uint4_t*>(xrow[i] + off + kk * 64);
   };
 
   int4_t acc[4][NT];
@@ -190,57 +258,73 @@ __global__ __launch_bounds__(256) void int8_gemm_kernel(Int8GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = int4_t{0, 0, 0, 0};
 
-  const int nk = a.k / IBK;
-  load_tile(0);
-  for (int ks = 0; ks < nk; ++ks) {
+  uint4_t wr[RB][4];
+  uint4_t ar[RA][2][4];
 #pragma unroll
-    for (int r = 0; r < AV; ++r) {
-      const int i = tid + 256 * r;
-      *reinterpret_cast<uint4_t*>(&As[(i >> 3) * ILD + (i & 7) * 16]) = ra[r];
-    }
+  for (int b = 0; b < RB; ++b) wload(wr[b], b);
 #pragma unroll
-    for (int r = 0; r < BVT; ++r) {
-      const int i = tid + 256 * r;
-      if (i < BV) *reinterpret_cast<uint4_t*>(&Bs[(i >> 3) * ILD + (i & 7) * 16]) = rb[r];
-    }
-    __syncthreads();
-    if (ks + 1 < nk) load_tile((ks + 1) * IBK);
+  for (int b = 0; b < RA; ++b) aload(ar[b], b);
+  wstore(wr[0], 0);
+  wload(wr[0], RB);
+  lgkm_wait0();
+  wg_barrier();
+
+  // step g (U = g % 4): weights of step g are in LDS buffer g & 1, those of
+  // step g + 1 in registers wr[(g + 1) % RB], activations in ar[g % RA]
+  auto step = [&](int g, auto uc) {
+    constexpr int U = decltype(uc)::value;
+    constexpr int WB = (U + 1) % RB;
+    wstore(wr[WB], (U + 1) & 1);   // step g + 1 (past the end: never read)
+    wload(wr[WB], g + 1 + RB);
+    const uint4_t* wc = wsl + (U & 1) * kI8WS;
 #pragma unroll
-    for (int kk = 0; kk < IBK / 64; ++kk) {
-      uint4_t af[4], bf[NT];
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + kc;
+      uint4_t bf[NT];   // all reads first: one LDS latency per half step
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const uint4_t*>(
-            &As[(wave * 64 + i * 16 + (lane & 15)) * ILD + kk * 64 + (lane >> 4) * 16]);
+      for (int j = 0; j < NT; ++j) {
+        const int r = j * 16 + nl;
+        bf[j] = wc[r * 8 + (c ^ i8_swz(r))];
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        bf[j] = *reinterpret_cast<const uint4_t*>(
-            &Bs[(j * 16 + (lane & 15)) * ILD + kk * 64 + (lane >> 4) * 16]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma_i8(af[i], bf[j], acc[i][j]);
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma_i8(ar[U % RA][kk][i], bf[j], acc[i][j]);
     }
-    __syncthreads();
+    aload(ar[U % RA], g + RA);
+    lgkm_wait0();   // this wave's LDS writes of step g + 1 ...
+    wg_barrier();   // ... and every wave's; every wave is done with buffer g & 1
+  };
+  // groups of four steps with no branch between them, so the compiler's
+  // load counting stays exact across the loop; then the last 0-3 steps
+  int g0 = 0;
+  for (; g0 + 4 <= nk; g0 += 4) {
+    step(g0, std::integral_constant<int, 0>{});
+    step(g0 + 1, std::integral_constant<int, 1>{});
+    step(g0 + 2, std::integral_constant<int, 2>{});
+    step(g0 + 3, std::integral_constant<int, 3>{});
   }
+  if (g0 < nk) step(g0, std::integral_constant<int, 0>{});
+  if (g0 + 1 < nk) step(g0 + 1, std::integral_constant<int, 1>{});
+  if (g0 + 2 < nk) step(g0 + 2, std::integral_constant<int, 2>{});
 
   // ---- epilogue: raw accumulators (optional), rescale, outlier slice
   float4_t yf[4][NT];
   float swv[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const int nn = n0 + j * 16 + (lane & 15);
+    const int nn = n0 + j * 16 + nl;
     swv[j] = nn < a.n ? a.sw[nn] : 0.0f;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int mm = m0 + wave * 64 + i * 16 + (lane >> 4) * 4 + e;
+      const int mm = m0 + wave * 64 + i * 16 + kc * 4 + e;
       const float sxv = mm < a.m ? a.sx[mm] : 0.0f;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int nn = n0 + j * 16 + (lane & 15);
+        const int nn = n0 + j * 16 + nl;
         if (a.acc_out != nullptr && mm < a.m && nn < a.n)
           a.acc_out[(int64_t)mm * a.n + nn] = acc[i][j][e];
         yf[i][j][e] = ((float)acc[i][j][e] * sxv) * swv[j];
@@ -249,36 +333,61 @@ __global__ __launch_bounds__(256) void int8_gemm_kernel(Int8GemmArgs a) {
   }
 
   const int cnt = *a.count;
-  uint16_t* Xo = reinterpret_cast<uint16_t*>(smem);              // [IBM][40] fp16
-  uint16_t* Wo = reinterpret_cast<uint16_t*>(smem) + IBM * 40;   // [BN][40] fp16
+  static_assert((kI8BM + 128) * 40 * 2 <= 2 * kI8WS * 16, "outlier staging fits");
+  uint16_t* Xo = reinterpret_cast<uint16_t*>(wsl);              // [256][40] fp16
+  uint16_t* Wo = reinterpret_cast<uint16_t*>(wsl) + kI8BM * 40;  // [BN][40] fp16
+  __shared__ int32_t sidx[32];
   for (int c0 = 0; c0 < cnt; c0 += 32) {
-    for (int e = tid; e < IBM * 32; e += 256) {
-      const int r = e >> 5, j = e & 31;
-      uint16_t v = 0;
-      if (c0 + j < cnt && m0 + r < a.m) v = a.x[(int64_t)(m0 + r) * a.k + a.idx[c0 + j]];
-      Xo[r * 40 + j] = v;
-    }
-    for (int e = tid; e < BN * 32; e += 256) {
-      const int r = e >> 5, j = e & 31;
-      uint16_t v = 0;
-      if (c0 + j < cnt && n0 + r < a.n) {
-        const float wq = (float)a.qw[(int64_t)(n0 + r) * a.k + a.idx[c0 + j]];
-        v = f32_to_f16_bits(as_f32(wq * a.sw[n0 + r]));
+    // the chunk's column indices once (-1 past the count); then every gather
+    // load of a thread is issued before any is used, so the chunk costs one
+    // memory latency rather than one per element
+    if (tid < 32) sidx[tid] = c0 + tid < cnt ? a.idx[c0 + tid] : -1;
+    __syncthreads();
+    {
+      // activations: thread t gathers row t of the tile, 32 columns
+      const bool rv = m0 + tid < a.m;
+      const uint16_t* xr = a.x + (int64_t)min(m0 + tid, a.m - 1) * a.k;
+      uint32_t v[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int c = sidx[j];
+        v[j] = (rv && c >= 0) ? (uint32_t)xr[c] : 0u;
       }
-      Wo[r * 40 + j] = v;
+#pragma unroll
+      for (int j = 0; j < 32; j += 2)
+        *reinterpret_cast<uint32_t*>(&Xo[tid * 40 + j]) = v[j] | (v[j + 1] << 16);
+    }
+    if (tid < 2 * BN) {
+      // weights: thread t gathers 16 columns (half t & 1) of row t >> 1,
+      // dequantized to fp16 as fp16(fp32(q) * sw)
+      const int r = tid >> 1, h = (tid & 1) * 16;
+      const bool rv = n0 + r < a.n;
+      const int nr = min(n0 + r, a.n - 1);
+      const int8_t* wrow = a.qw + (int64_t)nr * a.k;
+      const float sc = a.sw[nr];
+      float q[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int c = sidx[h + j];
+        q[j] = (rv && c >= 0) ? (float)wrow[c] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const uint32_t lo = f32_to_f16_bits(as_f32(q[j] * sc));
+        const uint32_t hi = f32_to_f16_bits(as_f32(q[j + 1] * sc));
+        *reinterpret_cast<uint32_t*>(&Wo[r * 40 + h + j]) = lo | (hi << 16);
+      }
     }
     __syncthreads();
-    uint4_t af[4];
+    uint4_t ao[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const uint4_t*>(
-          &Xo[(wave * 64 + i * 16 + (lane & 15)) * 40 + (lane >> 4) * 8]);
+      ao[i] = *reinterpret_cast<const uint4_t*>(&Xo[(wave * 64 + i * 16 + nl) * 40 + kc * 8]);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const uint4_t bf =
-          *reinterpret_cast<const uint4_t*>(&Wo[(j * 16 + (lane & 15)) * 40 + (lane >> 4) * 8]);
+      const uint4_t bo = *reinterpret_cast<const uint4_t*>(&Wo[(j * 16 + nl) * 40 + kc * 8]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yf[i][j] = mfma_f16(af[i], bf, yf[i][j]);
+      for (int i = 0; i < 4; ++i) yf[i][j] = mfma_f16(ao[i], bo, yf[i][j]);
     }
     __syncthreads();
   }
@@ -287,10 +396,10 @@ __global__ __launch_bounds__(256) void int8_gemm_kernel(Int8GemmArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int mm = m0 + wave * 64 + i * 16 + (lane >> 4) * 4 + e;
+      const int mm = m0 + wave * 64 + i * 16 + kc * 4 + e;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int nn = n0 + j * 16 + (lane & 15);
+        const int nn = n0 + j * 16 + nl;
         if (mm < a.m && nn < a.n) {
           if constexpr (YDT == WQ_F32)
             static_cast<float*>(a.y)[(int64_t)mm * a.n + nn] = yf[i][j][e];
@@ -301,21 +410,25 @@ __global__ __launch_bounds__(256) void int8_gemm_kernel(Int8GemmArgs a) {
     }
 }
 
+template <int NT>
+hipError_t launch_int8_gemm_nt(const Int8GemmArgs& a, int ydt, hipStream_t s) {
+  const dim3 grid((unsigned)((a.n + NT * 16 - 1) / (NT * 16)), (unsigned)((a.m + kI8BM - 1) / kI8BM));
+  if (ydt == WQ_F32)
+    int8_gemm_kernel<NT, WQ_F32><<<grid, 256, 0, s>>>(a);
+  else
+    int8_gemm_kernel<NT, WQ_F16><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_int8_prepare(const uint16_t* x, int64_t m, int64_t k, float thr,
                                uint8_t* mask, int32_t* idx, int32_t* count, int8_t* qx,
                                float* sx, hipStream_t s) {
-  // The per-row-chunk column flags (chunks * k bytes) are staged in qx, which
-  // holds m * k >= chunks * k bytes and is overwritten by int8_quant_act after
-  // int8_compact has consumed them (same stream, in order).
-  const int chunks = (int)((m + kRowChunk - 1) / kRowChunk);
-  uint8_t* flags = reinterpret_cast<uint8_t*>(qx);
-  int8_colflags_kernel<<<dim3((unsigned)((k + 255) / 256), (unsigned)chunks), 256, 0, s>>>(
-      x, m, k, thr, flags);
+  int8_colmask_kernel<<<dim3((unsigned)((k + 63) / 64)), 256, 0, s>>>(x, m, k, thr, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int8_compact_kernel<<<1, 1024, 0, s>>>(flags, k, chunks, mask, idx, count);
+  int8_compact_kernel<<<1, 1024, 0, s>>>(mask, k, idx, count);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   int8_quant_act_kernel<<<dim3((unsigned)m), 256, 0, s>>>(x, k, mask, qx, sx);
@@ -338,13 +451,12 @@ hipError_t launch_int8_gemm(const uint16_t* x, int64_t m, const wq_weight* w, co
   a.k = (int)w->k;
   a.y = y;
   a.acc_out = acc_out;
-  constexpr int NT = 8;
-  const dim3 grid((unsigned)((w->n + NT * 16 - 1) / (NT * 16)), (unsigned)((m + IBM - 1) / IBM));
-  if (ydt == WQ_F32)
-    int8_gemm_kernel<NT, WQ_F32><<<grid, 256, 0, s>>>(a);
-  else
-    int8_gemm_kernel<NT, WQ_F16><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  // tile width 112 or 128: the one with less work per CU over the rounds of
+  // 256 workgroups (one per CU) the grid takes; ties go to 112 (more CUs)
+  const int64_t ntm = (m + kI8BM - 1) / kI8BM;
+  auto rounds = [&](int64_t bn) { return ((w->n + bn - 1) / bn * ntm + 255) / 256; };
+  if (rounds(112) * 7 <= rounds(128) * 8) return launch_int8_gemm_nt<7>(a, ydt, s);
+  return launch_int8_gemm_nt<8>(a, ydt, s);
 }
 
 }  // namespace wq

@@ -177,46 +177,6 @@ __device__ __forceinline__ uint4_t dequant_nf4_word(uint32_t w, const float* lut
   return b;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's 16 bytes land at lds + 16*l (lds is wave-uniform, passed in M0).
-// Issued from inline asm on purpose: the compiler's wait-count bookkeeping
-// treats these loads as completing out of order with ordinary loads and then
-// falls back to waiting for every outstanding load.  Hidden from it, its
-// automatic waits for ordinary loads count only ordinary loads, which can
-// only make them stricter (each direct load it does not see is one more
-// outstanding load that must finish first); the kernels wait for their
-// direct loads themselves (vm_wait with counts that include them) before any
-// LDS read of the data.  No output register, so nothing is left in flight
-// behind the compiler's back but LDS bytes the explicit waits cover.  The
-// s_nop is the one wait state an LDS-DMA instruction needs after a scalar
-// write of M0, which the compiler pads for its own such loads but cannot
-// see here.
-__device__ __forceinline__ void lds_dma16(const void* gaddr, lds_void_t* lds) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(l) : "memory");
-}
-
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima, i.e. no wait).
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  constexpr int n = N > 63 ? 63 : N;
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads(): the fence
-// would make every wave wait for all of its outstanding global loads (the
-// direct-to-LDS loads are counted with them), which serializes the weight
-// stream behind the first phase.  Callers wait for exactly the loads that
-// must have landed (vm_wait) before calling it; the empty asm statements keep
-// the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // s_waitcnt vmcnt(n) for a wave-uniform count known only at run time, by
 // binary search over the immediates (counts above the hardware maximum wait
 // for that maximum, which waits for more loads than asked: safe).

@@ -71,6 +71,8 @@ def run_decomp(x_np, w_np, thr, ydt):
     (300, 200, 512, 5, 6.0, "f32"),       # two 256-row tiles
     (16, 256, 1024, 4, float("inf"), "f32"),
     (16, 128, 256, 2, 0.0, "f32"),
+    (512, 1000, 640, 3, 6.0, "f32"),      # two full 256-row tiles, 112-wide column tiles, ragged n
+    (16, 28688, 256, 2, 6.0, "f16"),      # 128-wide column tiles (112 would need a second round)
 ])
 def test_decomp_parity(m, n, k, n_out, thr, ydt):
     say(f"int8_decomp m={m} n={n} k={k} outliers={n_out} thr={thr} y={ydt}")

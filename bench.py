@@ -464,6 +464,50 @@ def summarize_pmc(fetch_csv, write_csv, kernel_substr, copy_mib, out_path, comma
     print(open(out_path).read())
 
 
+def summarize_counters(csv_paths, kernel_substr, avg_ns, out_path, command):
+    """Write the mean per-dispatch value of every counter in one or more
+    rocprofv3 --pmc runs for the kernels matching NAME[@GRID_WORK_ITEMS],
+    with the matrix-core busy share derived from them.  avg_ns is the
+    kernel's average duration (from the kernel trace of the same command),
+    used for the effective clock."""
+    import csv
+    import statistics
+    name_substr, _, grid = kernel_substr.partition("@")
+    vals = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            if name_substr not in r["Kernel_Name"] or (grid and r["Grid_Size"] != grid):
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = {k: statistics.mean(v) for k, v in vals.items()}
+    with open(out_path, "w") as f:
+        f.write(f"# rocprofv3 counters, mean per dispatch, kernels matching '{kernel_substr}'\n")
+        f.write(f"# command: {command}\n")
+        for k in sorted(mean):
+            f.write(f"{k}={mean[k]:.6g}  # {len(vals[k])} dispatches\n")
+        if "GRBM_GUI_ACTIVE" in mean and avg_ns > 0:
+            # GRBM_GUI_ACTIVE is summed over the 8 XCDs; SQ_* counters over
+            # every CU (256) and SIMD (4 per CU)
+            cyc = mean["GRBM_GUI_ACTIVE"] / 8.0
+            f.write(f"# derived: active cycles per XCD {cyc:.0f}; effective clock "
+                    f"{cyc / avg_ns:.3f} GHz over a {avg_ns / 1e3:.2f} us dispatch\n")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                f.write(f"mfma_busy_share={mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024.0 * cyc):.4f}"
+                        "  # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x active cycles)\n")
+            if "SQ_LDS_BANK_CONFLICT" in mean:
+                f.write(f"lds_bank_conflict_share={mean['SQ_LDS_BANK_CONFLICT'] / (256.0 * cyc):.4f}"
+                        "  # SQ_LDS_BANK_CONFLICT / (256 CUs x active cycles)\n")
+            if "TCP_PENDING_STALL_CYCLES" in mean:
+                f.write(f"l1_pending_stall_share={mean['TCP_PENDING_STALL_CYCLES'] / (256.0 * cyc):.4f}"
+                        "  # TCP_PENDING_STALL_CYCLES / (256 CUs x active cycles)\n")
+        if "TCP_TCC_READ_REQ" in mean and "TCP_TCC_READ_REQ_LATENCY" in mean:
+            f.write(f"l1_to_l2_read_latency_cycles="
+                    f"{mean['TCP_TCC_READ_REQ_LATENCY'] / mean['TCP_TCC_READ_REQ']:.1f}\n")
+        if "TCC_HIT" in mean and "TCC_MISS" in mean:
+            f.write(f"l2_hit_rate={mean['TCC_HIT'] / (mean['TCC_HIT'] + mean['TCC_MISS']):.4f}\n")
+    print(open(out_path).read())
+
+
 def summarize_trace(prof_dir, bench_json, title, out_path, command):
     """Write a rocprofv3 --kernel-trace --stats summary: per kernel and
     launch grid (one grid per layer shape), the calls and the average /
@@ -508,6 +552,11 @@ def main():
         # --summarize-pmc FETCH_CSV WRITE_CSV KERNEL_SUBSTR COPY_MIB OUT "COMMAND"
         a = sys.argv[2:]
         summarize_pmc(a[0], a[1], a[2], int(a[3]), a[4], a[5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # --summarize-counters KERNEL[@GRID] AVG_NS OUT "COMMAND" CSV [CSV ...]
+        a = sys.argv[2:]
+        summarize_counters(a[4:], a[0], float(a[1]), a[2], a[3])
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)

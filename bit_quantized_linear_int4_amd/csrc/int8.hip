@@ -161,12 +161,6 @@ constexpr int kI8WS = 128 * kI8BK / 16;      // 16-byte slots per weight buffer 
 
 __device__ __forceinline__ int i8_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima): this wave's
-// LDS writes are done
-__device__ __forceinline__ void lgkm_wait0() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-}
-
 __device__ __forceinline__ int4_t mfma_i8(uint4_t a, uint4_t b, int4_t c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int4_t, a),
                                                __builtin_bit_cast(int4_t, b), c, 0, 0, 0);

@@ -85,6 +85,12 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maxima): this wave's
+// LDS writes are done
+__device__ __forceinline__ void lgkm_wait0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would make every wave wait for all of its outstanding global loads (the
 // direct-to-LDS loads are counted with them), which serializes the weight

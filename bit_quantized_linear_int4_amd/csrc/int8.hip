@@ -9,10 +9,11 @@
 //
 // Kernels, in launch order:
 //   int8_colmask    per column: any |x| > threshold over the rows -> mask
-//   int8_compact    one workgroup: mask -> ascending outlier list, count (no
-//                   host round trip; the count stays on the device)
 //   int8_quant_act  one workgroup per token: absmax over the non-outlier
-//                   columns -> sx, codes (0 in outlier columns)
+//                   columns -> sx, codes (0 in outlier columns); one more
+//                   workgroup compacts the mask into the ascending outlier
+//                   list and its count (no host round trip; the count stays
+//                   on the device)
 //   int8_gemm       256 x BN output tiles: v_mfma_i32_16x16x64_i8 over K, then
 //                   y = acc * sx * sw, then the outlier columns through
 //                   v_mfma_f32_16x16x32_f16 on fp16 activations and the int8
@@ -56,39 +57,58 @@ __global__ __launch_bounds__(256) void int8_colmask_kernel(const uint16_t* __res
   }
 }
 
-// One workgroup: ascending list of the flagged columns and their count (no
-// host round trip; the count stays on the device).
-__global__ __launch_bounds__(1024) void int8_compact_kernel(const uint8_t* __restrict__ mask,
-                                                            int64_t k,
-                                                            int32_t* __restrict__ idx,
-                                                            int32_t* __restrict__ count) {
-  __shared__ int32_t part[1024];
+// Ascending list of the flagged columns and their count, by one workgroup
+// of 256 threads (no host round trip; the count stays on the device).  The
+// mask bytes are 0 or 1; each thread reads a contiguous run of 16-byte
+// chunks (k % 16 == 0, mask 16-byte aligned), counts them with popcounts,
+// and an exclusive scan of the counts gives its first output position.
+__device__ void compact_mask(const uint8_t* __restrict__ mask, int64_t k,
+                             int32_t* __restrict__ idx, int32_t* __restrict__ count,
+                             int32_t* part) {
   const int t = threadIdx.x;
-  const int64_t per = (k + 1023) / 1024;
-  const int64_t c0 = std::min<int64_t>(k, t * per), c1 = std::min<int64_t>(k, c0 + per);
+  const int64_t chunks = k / 16, per = (chunks + 255) / 256;
+  const int64_t c0 = std::min<int64_t>(chunks, t * per), c1 = std::min<int64_t>(chunks, c0 + per);
+  const uint4_t* m16 = reinterpret_cast<const uint4_t*>(mask);
   int32_t n = 0;
-  for (int64_t c = c0; c < c1; ++c) n += mask[c];
+  for (int64_t c = c0; c < c1; ++c) {
+    const uint4_t v = m16[c];
+    n += __popc(v[0]) + __popc(v[1]) + __popc(v[2]) + __popc(v[3]);
+  }
   part[t] = n;
   __syncthreads();
-  // inclusive scan (Hillis-Steele) over 1024 partial counts
-  for (int off = 1; off < 1024; off <<= 1) {
+  // inclusive scan (Hillis-Steele) over 256 partial counts
+  for (int off = 1; off < 256; off <<= 1) {
     const int32_t v = t >= off ? part[t - off] : 0;
     __syncthreads();
     part[t] += v;
     __syncthreads();
   }
   int32_t pos = part[t] - n;
-  for (int64_t c = c0; c < c1; ++c)
-    if (mask[c]) idx[pos++] = (int32_t)c;
-  if (t == 1023) *count = part[1023];
+  for (int64_t c = c0; c < c1; ++c) {
+    const uint4_t v = m16[c];
+    if ((v[0] | v[1] | v[2] | v[3]) == 0u) continue;
+#pragma unroll
+    for (int b = 0; b < 16; ++b)
+      if ((v[b >> 2] >> (8 * (b & 3))) & 1u) idx[pos++] = (int32_t)(c * 16 + b);
+  }
+  if (t == 255) *count = part[255];
 }
 
+// One workgroup per token row; one more workgroup (the last) compacts the
+// mask meanwhile.
 __global__ __launch_bounds__(256) void int8_quant_act_kernel(const uint16_t* __restrict__ x,
                                                              int64_t k,
                                                              const uint8_t* __restrict__ mask,
                                                              int8_t* __restrict__ qx,
-                                                             float* __restrict__ sx) {
+                                                             float* __restrict__ sx,
+                                                             int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ count) {
   __shared__ float red[4];
+  __shared__ int32_t part[256];
+  if (blockIdx.x == gridDim.x - 1) {
+    compact_mask(mask, k, idx, count, part);
+    return;
+  }
   const int64_t row = blockIdx.x;
   const uint16_t* xr = x + row * k;
   const int64_t chunks = k / 8;
@@ -422,10 +442,7 @@ hipError_t launch_int8_prepare(const uint16_t* x, int64_t m, int64_t k, float th
   int8_colmask_kernel<<<dim3((unsigned)((k + 63) / 64)), 256, 0, s>>>(x, m, k, thr, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int8_compact_kernel<<<1, 1024, 0, s>>>(mask, k, idx, count);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  int8_quant_act_kernel<<<dim3((unsigned)m), 256, 0, s>>>(x, k, mask, qx, sx);
+  int8_quant_act_kernel<<<dim3((unsigned)(m + 1)), 256, 0, s>>>(x, k, mask, qx, sx, idx, count);
   return hipGetLastError();
 }
 

@@ -251,8 +251,8 @@ wq_status wq_int8_prepare_activations(const void* x, int64_t m, int64_t k, float
     return WQ_ERR_NULL;
   if (!sizes_ok(m, k) || k % 16 != 0) return WQ_ERR_SHAPE;
   if (!(threshold >= 0.0f)) return WQ_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(idx, 4) || !aligned(count, 4) ||
-      !aligned(sx, 4))
+  if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(mask, 16) || !aligned(idx, 4) ||
+      !aligned(count, 4) || !aligned(sx, 4))
     return WQ_ERR_ALIGN;
   return hip_status(launch_int8_prepare(static_cast<const uint16_t*>(x), m, k, threshold, mask,
                                         idx, count, qx, sx, static_cast<hipStream_t>(stream)));

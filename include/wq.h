@@ -254,9 +254,9 @@ wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
  *     *count = |O| (device int32).
  *   per row i: sx[i] = max_{c not in O} |x[i][c]| / 127 (1.0 if 0),
  *     qx[i][c] = clamp(round(x[i][c] / sx[i]), -127, 127), 0 for c in O.
- * x: fp16 [m][k], 16-byte aligned, k % 16 == 0.  mask uint8 [k],
- * idx int32 [k], count int32 [1], qx int8 [m][k] (16-byte aligned), sx fp32
- * [m].  threshold >= 0 (use +inf for no outliers).
+ * x: fp16 [m][k], 16-byte aligned, k % 16 == 0.  mask uint8 [k] (16-byte
+ * aligned), idx int32 [k], count int32 [1], qx int8 [m][k] (16-byte
+ * aligned), sx fp32 [m].  threshold >= 0 (use +inf for no outliers).
  */
 wq_status wq_int8_prepare_activations(const void* x, int64_t m, int64_t k,
                                       float threshold, uint8_t* mask,

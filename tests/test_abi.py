@@ -252,6 +252,7 @@ def test_int8_argument_errors():
     p = _lib().wq_int8_prepare_activations
     assert p(A16, 4, 256, 6.0, A16, A16, A16, None, A16, None) == NULL
     assert p(A16, 4, 250, 6.0, A16, A16, A16, A16, A16, None) == SHAPE
+    assert p(A16, 4, 256, 6.0, A16 + 4, A16, A16, A16, A16, None) == ALIGN
 
 
 def test_dequantize_argument_errors():

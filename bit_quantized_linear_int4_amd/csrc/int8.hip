@@ -160,10 +160,9 @@ __global__ __launch_bounds__(256) void int8_quant_act_kernel(const uint16_t* __r
 // so the int8 weights stream from HBM once; the activation codes (at most a
 // few MB) are re-read from L2 by every tile.
 //
-//  * Every load lands in registers (global_load_dwordx4): on this GPU a CU
-//    streams about a fifth more through ordinary vector loads than through
-//    direct global->LDS loads, and the compiler then counts every load in its
-//    own waits.
+//  * Every load lands in registers (global_load_dwordx4), so the compiler
+//    counts every load in its own waits.  (The direct global->LDS version
+//    of this kernel took 125 us on the 70B layer, this one 94-108 us.)
 //  * A wave's activation rows are its own: they are loaded straight into
 //    the MFMA A-operand registers, two steps ahead (RA = 2 register stages).
 //  * The weight slice of a step is shared by the four waves: each thread

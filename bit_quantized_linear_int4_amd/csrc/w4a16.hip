@@ -90,6 +90,25 @@ __device__ __forceinline__ uint16_t f32_to_x(float v) {
   return XDT == WQ_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
 }
 
+// Two fp32 values -> two 16-bit values of the activation type in one word
+// (low half = v0), each rounded to nearest even once (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32).
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int XDT>
+__device__ __forceinline__ uint32_t pack2_x(float v0, float v1) {
+  const float2_t v = {v0, v1};
+  uint32_t u;
+  if constexpr (XDT == WQ_BF16) {
+    const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+    __builtin_memcpy(&u, &b, 4);
+  } else {
+    const half2_t h = __builtin_convertvector(v, half2_t);
+    __builtin_memcpy(&u, &h, 4);
+  }
+  return u;
+}
+
 template <int YDT>
 __device__ __forceinline__ void store_y(void* y, int64_t idx, float v) {
   if constexpr (YDT == WQ_F32) {
@@ -740,8 +759,15 @@ constexpr int kGemmWaves = WQ_GEMM_WAVES;   // 4: 128 x 64 per wave; 8: 128 x 32
 constexpr int kGemmScaleBytes = 256 * kGemmMaxGroups * 2;
 constexpr int kGemmZeroBytes = 256 * kGemmMaxGroups / 2;
 
-template <int YDT, int NWG, int SUB>   // SUB: INT4 groups per unit of 128 (1, 2, 4)
-__global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
+// FMT/XDT: INT4 with fp16 activations takes the exponent-bias dequant above;
+// INT4 with bf16 activations and NF4/FP4 (double-quantized absmax) take the
+// exact general one: each weight is formed in fp32 ((q - z) * s, exact; or
+// level * absmax, rounded once) and rounded once into the activation type
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), as the dequantization defines.
+template <int FMT, int XDT, int YDT, int NWG, int SUB>   // SUB: INT4 groups per unit of 128 (1, 2, 4)
+__global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv) {
+  constexpr bool FAST = FMT == WQ_FMT_INT4_ASYM && XDT == WQ_F16;
+  static_assert(FMT == WQ_FMT_INT4_ASYM || SUB == 1, "NF4 blocks: one unit of 128 = two blocks");
   constexpr int NW = NWG, BM = 128, BN = 256;
   constexpr int NF = BN / 16 / NW;               // 16-row code tiles per wave (n)
   constexpr int XBUF = BM * 16;                  // 16-byte chunks per activation buffer
@@ -777,9 +803,34 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
   const int ZCB = (BN * a.zb + 1023) / 1024 * 1024;
   const int lq = (kq * SUB) >> 2;                // this lane's group within a unit
 
-  // staged scales and zero points of rows n0 .. n0+255 (clamped at the end
-  // of the buffers; rows past n are never stored)
-  {
+  // NF4: the 16 levels, and the second-level scales of the tile's blocks
+  // (rows n0 .. n0+255 hold blocks n0*k/64 .. (n0+256)*k/64 - 1; their
+  // scales2 indices start at c2b), written before any direct load is issued
+  // so the compiler's wait for these loads waits for nothing else
+  // lut2[b] = (level of code b & 15, level of code b >> 4): one 8-byte
+  // read per byte of codes
+  __shared__ float2_t lut2[FMT != WQ_FMT_INT4_ASYM ? 256 : 1];
+  const int bpr = a.k / 64;                      // NF4 blocks per row
+  const int64_t c2b = ((int64_t)n0 * bpr) >> 8;
+  if constexpr (FMT != WQ_FMT_INT4_ASYM) {
+    float* c2s = reinterpret_cast<float*>(zcl);
+    const int nc2 = (int)((((int64_t)min(n0 + BN, a.n) * bpr - 1) >> 8) - c2b + 1);
+    if (tid < 256) lut2[tid] = float2_t{lv.v[tid & 15], lv.v[tid >> 4]};
+    for (int i = tid; i < nc2; i += NW * 64) c2s[i] = a.scales2[c2b + i];
+    lgkm_wait0();
+  }
+  // staged scales and zero points of rows n0 .. n0+255 (NF4: the int8
+  // absmax codes of their blocks), clamped at the end of the buffers; rows
+  // past n are never stored
+  if constexpr (FMT != WQ_FMT_INT4_ASYM) {
+    const int nab = (BN * bpr + 1023) / 1024;
+    const int64_t abytes = (int64_t)a.n * bpr;
+    for (int i = wave; i < nab; i += NW) {
+      const int64_t off = (int64_t)n0 * bpr + i * 1024 + lane * 16;
+      lds_dma16(static_cast<const uint8_t*>(a.scales) + min(off, abytes - 16),
+                (lds_void_t*)(scl + i * 1024));
+    }
+  } else {
     const int nsc = SCB / 1024, nzc = ZCB / 1024;
     const int64_t sbytes = (int64_t)a.n * GS * 2, zbytes = (int64_t)a.n * a.zb;
     for (int i = wave; i < nsc + nzc; i += NW) {
@@ -848,20 +899,34 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
     issue_w(g + 2);
     const uint4_t* xcur = xr + (g & 1) * XBUF;
     const uint4_t* wcur = wr + (g % 3) * WBUF;
-    // codes, scales and zero points of this wave's 4 row tiles for group g
+    // codes, scales and zero points (NF4: absmax) of this wave's row tiles
+    // for group g
     uint4_t wv[NF];
     half2_t s2[NF], nz2[NF];
+    float sf[NF], zf[NF];   // INT4: s and -z * s (exact); NF4: absmax, unused
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int r = wn * 16 * NF + j * 16 + nl;
       wv[j] = wcur[r * 4 + (kq ^ ((r >> 2) & 3))];
-      const int gq = g * SUB + lq;
-      _Float16 sc16;
-      __builtin_memcpy(&sc16, scl + (r * GS + gq) * 2, 2);
-      const uint32_t zb = zcl[r * a.zb + (gq >> 1)];
-      const float z = (float)((gq & 1) ? (zb >> 4) : (zb & 15u));
-      s2[j] = half2_t{sc16, sc16};
-      nz2[j] = half2_t{(_Float16)(-(1024.0f + z)), (_Float16)(-(64.0f + z))};
+      if constexpr (FMT == WQ_FMT_INT4_ASYM) {
+        const int gq = g * SUB + lq;
+        _Float16 sc16;
+        __builtin_memcpy(&sc16, scl + (r * GS + gq) * 2, 2);
+        const uint32_t zb = zcl[r * a.zb + (gq >> 1)];
+        const float z = (float)((gq & 1) ? (zb >> 4) : (zb & 15u));
+        s2[j] = half2_t{sc16, sc16};
+        nz2[j] = half2_t{(_Float16)(-(1024.0f + z)), (_Float16)(-(64.0f + z))};
+        sf[j] = (float)sc16;
+        zf[j] = -z * sf[j];
+      } else {
+        // absmax of this lane's block (quarter kq of the unit lies in block
+        // 2g + kq/2 of the row): fp32(q8) * c2, as the double quantization
+        // defines it
+        const int bl = r * bpr + 2 * g + (kq >> 1);
+        const float c2 = reinterpret_cast<const float*>(zcl)[(((int64_t)n0 * bpr + bl) >> 8) - c2b];
+        sf[j] = (float)reinterpret_cast<const int8_t*>(scl)[bl] * c2;
+        zf[j] = 0.0f;
+      }
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -874,18 +939,34 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
         uint4_t B;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t u = and_or(__builtin_amdgcn_perm(w, w, 0x01010101u * e), kMask, kBias);
-          // through scalar copies: a bit_cast straight from a vector element
-          // produced wrong code here
-          half2_t h;
-          __builtin_memcpy(&h, &u, 4);
-          h = (h + nz2[j]) * s2[j];
-          uint32_t be;
-          __builtin_memcpy(&be, &h, 4);
-          B[e] = be;
+          if constexpr (FAST) {
+            const uint32_t u = and_or(__builtin_amdgcn_perm(w, w, 0x01010101u * e), kMask, kBias);
+            // through scalar copies: a bit_cast straight from a vector element
+            // produced wrong code here
+            half2_t h;
+            __builtin_memcpy(&h, &u, 4);
+            h = (h + nz2[j]) * s2[j];
+            uint32_t be;
+            __builtin_memcpy(&be, &h, 4);
+            B[e] = be;
+          } else {
+            float v0, v1;
+            if constexpr (FMT == WQ_FMT_INT4_ASYM) {
+              // q * s - z * s in one fma: (q - z) * s is exact in fp32, so
+              // the single rounding of the fma changes nothing
+              const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+              v0 = fmaf((float)((lo >> (8 * e)) & 255u), sf[j], zf[j]);
+              v1 = fmaf((float)((hi >> (8 * e)) & 255u), sf[j], zf[j]);
+            } else {
+              const float2_t l = lut2[(w >> (8 * e)) & 255u];
+              v0 = as_f32(l.x * sf[j]);
+              v1 = as_f32(l.y * sf[j]);
+            }
+            B[e] = pack2_x<XDT>(v0, v1);
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i][j] = mfma16<WQ_F16>(A[i], B, acc[i][j]);
+        for (int i = 0; i < 8; ++i) acc[i][j] = mfma16<XDT>(A[i], B, acc[i][j]);
       }
     }
   }
@@ -903,8 +984,8 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a) {
       }
 }
 
-template <int YDT>
-hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
+template <int FMT, int XDT, int YDT>
+hipError_t launch_gemm_i4(const GemmArgs& a, const Levels& lv, hipStream_t s) {
   constexpr int NWG = kGemmWaves;
   // one launch per slice of rows keeps the 1-D grid within 2^22 workgroups
   const int64_t ntn = (a.n + 255) / 256, ysz = YDT == WQ_F32 ? 4 : 2;
@@ -915,12 +996,16 @@ hipError_t launch_gemm_i4(const GemmArgs& a, hipStream_t s) {
     b.x = a.x + r0 * a.k;
     b.y = static_cast<char*>(a.y) + r0 * a.n * ysz;
     const dim3 grid((unsigned)(ntn * ((b.m + 127) / 128)));
-    if (a.sub == 4)
-      gemm_i4_kernel<YDT, NWG, 4><<<grid, NWG * 64, 0, s>>>(b);
-    else if (a.sub == 2)
-      gemm_i4_kernel<YDT, NWG, 2><<<grid, NWG * 64, 0, s>>>(b);
-    else
-      gemm_i4_kernel<YDT, NWG, 1><<<grid, NWG * 64, 0, s>>>(b);
+    if constexpr (FMT != WQ_FMT_INT4_ASYM) {
+      gemm_i4_kernel<FMT, XDT, YDT, NWG, 1><<<grid, NWG * 64, 0, s>>>(b, lv);
+    } else {
+      if (a.sub == 4)
+        gemm_i4_kernel<FMT, XDT, YDT, NWG, 4><<<grid, NWG * 64, 0, s>>>(b, lv);
+      else if (a.sub == 2)
+        gemm_i4_kernel<FMT, XDT, YDT, NWG, 2><<<grid, NWG * 64, 0, s>>>(b, lv);
+      else
+        gemm_i4_kernel<FMT, XDT, YDT, NWG, 1><<<grid, NWG * 64, 0, s>>>(b, lv);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1051,8 +1136,14 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
     a.sub = a.GS / a.G;
     a.zb = (a.GS + 1) / 2;
     a.y = y;
-    if (XDT == WQ_F16 && w->fmt == WQ_FMT_INT4_ASYM && p.szl && a.GS <= kGemmMaxGroups)
-      return launch_gemm_i4<YDT>(a, s);
+    if (w->fmt == WQ_FMT_INT4_ASYM && p.szl && a.GS <= kGemmMaxGroups)
+      return launch_gemm_i4<WQ_FMT_INT4_ASYM, XDT, YDT>(a, lv, s);
+    // NF4/FP4 with double-quantized absmax: the int8 codes of a tile's 256
+    // rows (256 * k/64 bytes) are staged in the scale buffer, so k <= 8192,
+    // staged by 16-byte direct loads (aligned buffer, size a multiple of 16)
+    if (w->fmt == WQ_FMT_NF4 && w->scales2 != nullptr && w->k <= 64 * kGemmMaxGroups * 2 &&
+        ((uintptr_t)w->scales % 16) == 0 && (w->n * (w->k / 64)) % 16 == 0)
+      return launch_gemm_i4<WQ_FMT_NF4, XDT, YDT>(a, lv, s);
     const dim3 grid((unsigned)((w->n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
     if (w->fmt == WQ_FMT_NF4)
       gemm_kernel<WQ_FMT_NF4, XDT, YDT><<<grid, 256, 0, s>>>(a, lv);

@@ -93,8 +93,13 @@ def run(x, w, xdt, ydt, dq=True, qw=None):
     (16, 512, 2048, "bf16", "f32", True),
     (1, 208, 11008, "bf16", "f32", True),
     (9, 160, 5120, "bf16", "f32", False),
-    (40, 300, 1152, "bf16", "f32", True),
+    (40, 300, 1152, "bf16", "f32", True),   # absmax not stageable: the generic GEMM
     (512, 1024, 4096, "bf16", "f32", True),
+    (40, 296, 1152, "bf16", "f32", True),   # staged absmax, ragged m and n tiles
+    (64, 256, 2048, "f16", "bf16", True),   # fp16 activations
+    (24, 128, 8192, "bf16", "f32", True),   # 32 KB of staged absmax codes: the limit
+    (20, 160, 8320, "bf16", "f32", True),   # past it: the generic GEMM
+    (40, 296, 1152, "bf16", "f32", False),  # fp32 absmax: the generic GEMM
 ])
 def test_linear_nf4_parity(m, n, k, xdt, ydt, dq):
     say(f"linear_nf4 m={m} n={n} k={k} x={xdt} y={ydt} dq={dq}")
@@ -170,6 +175,8 @@ def test_dequantize_fp4_bitexact(dq, odt):
     (16, 512, 2048, "bf16", "f32", True),
     (40, 300, 1152, "bf16", "f32", True),
     (512, 1024, 4096, "bf16", "f32", True),
+    (40, 296, 1152, "bf16", "f32", True),   # staged absmax, ragged m and n tiles
+    (72, 512, 2048, "f16", "f32", True),    # fp16 activations
 ])
 def test_linear_fp4_parity(m, n, k, xdt, ydt, dq):
     say(f"linear_fp4 m={m} n={n} k={k} x={xdt} y={ydt} dq={dq}")

@@ -227,6 +227,7 @@ def test_gate_up_swiglu_parity(m, n, k, ydt):
     (300, 1024, 2048, "f16", "f16", 32),  # GEMM, 64 groups: the staging limit
     (130, 272, 4096, "f16", "f32", 32),   # 128 groups: the generic GEMM
     (200, 520, 1024, "bf16", "f32", 64),
+    (130, 264, 2048, "bf16", "bf16", 32),  # bf16 GEMM, four groups per unit, ragged tiles
 ])
 def test_linear_group_sizes(m, n, k, xdt, ydt, group):
     """Groups of 64 and 32 ([P5] 2.2 group-wise granularity, the group-size

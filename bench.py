@@ -90,7 +90,7 @@ class W4Layers(Workload):
         import torch
         import bit_quantized_linear_int4_amd as wq
         self.wq = wq
-        base, self.xs, self.ys = [], [], []
+        base, self.xs, self.ys, self.wss = [], [], [], []
         bytes_, flops = [], []
         for _, x, w in self.layers_np:
             qw = _int4_weight(wq, torch, w)
@@ -100,7 +100,9 @@ class W4Layers(Workload):
             self.ys.append(torch.empty((m, n), dtype=torch.float16, device="cuda"))
             bytes_.append(qw.nbytes() + x.size * 2 + m * n * 2)
             flops.append(2 * m * n * k)
-            assert wq.wq_linear_w4a16_workspace(m, qw) == 0
+            # scratch of a K-split schedule (partial sums; not algorithmic bytes)
+            need = wq.wq_linear_w4a16_workspace(m, qw)
+            self.wss.append(torch.empty((need,), dtype=torch.uint8, device="cuda") if need else None)
         torch.cuda.synchronize()
         reps = _copies_needed(sum(q.nbytes() for q in base))
         self.copies = [base] + [[q.clone() for q in base] for _ in range(reps - 1)]
@@ -144,7 +146,7 @@ class W4Layers(Workload):
             return lambda: wq.wq_linear_w4a16_gate_up(self.xs[i], ws[i], ws[j], self.ys[i],
                                                       self.ys[j], act=0)
         i = u[0]
-        return lambda: wq.wq_linear_w4a16(self.xs[i], ws[i], self.ys[i], None)
+        return lambda: wq.wq_linear_w4a16(self.xs[i], ws[i], self.ys[i], self.wss[i])
 
     def step_calls(self, copy):
         return [self._call(copy, ui) for ui in range(len(self.units))]

@@ -246,7 +246,10 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   constexpr bool CRING = SZL && !DUAL;
   constexpr int CG = NW * GPP;                             // groups per phase
   constexpr int XS = (MP * GPP * 16 + 63) / 64 * 64;       // slots per wave buffer
-  constexpr int XI = XS / 64;                              // direct loads per phase
+  // direct activation loads per phase: 1 KB each, or with one staged row
+  // (MP = 1) one 256-byte load per group (lane l: 4 bytes at 4 l), so a
+  // phase moves the row's 256 bytes instead of a KB of duplicates
+  constexpr int XI = MP == 1 ? GPP : XS / 64;
   constexpr int LPU = SZL ? 1 : 3;                         // loads per code unit
   constexpr int WU = TPG * GPP * LPU;                      // code-side loads per phase
   constexpr bool FAST = (FMT == WQ_FMT_INT4_ASYM) && (XDT == WQ_F16);
@@ -310,6 +313,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // read clamped addresses and are never used
   auto issue_x = [&](int p) {
     uint4_t* buf = ring + (p % NBUF) * XS;
+    if constexpr (MP == 1) {
+#pragma unroll
+      for (int gl = 0; gl < GPP; ++gl) {
+        const int g = min(gbeg + p * CG + wave * GPP + gl, a.G - 1);
+        lds_dma4(a.x + g * 128 + lane * 2, (lds_void_t*)(buf + gl * 16));
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int sl = i * 64 + lane;

@@ -491,8 +491,9 @@ def summarize_counters(csv_paths, kernel_substr, avg_ns, out_path, command):
             # GRBM_GUI_ACTIVE is summed over the 8 XCDs; SQ_* counters over
             # every CU (256) and SIMD (4 per CU)
             cyc = mean["GRBM_GUI_ACTIVE"] / 8.0
-            f.write(f"# derived: active cycles per XCD {cyc:.0f}; effective clock "
-                    f"{cyc / avg_ns:.3f} GHz over a {avg_ns / 1e3:.2f} us dispatch\n")
+            f.write(f"# derived: active cycles per XCD {cyc:.0f} (GRBM_GUI_ACTIVE / 8); over the "
+                    f"traced {avg_ns / 1e3:.2f} us dispatch that is {cyc / avg_ns:.3f} GHz, an upper "
+                    "bound on the clock (counter runs lengthen dispatches)\n")
             if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
                 f.write(f"mfma_busy_share={mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024.0 * cyc):.4f}"
                         "  # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x active cycles)\n")

@@ -1121,6 +1121,7 @@ hipError_t launch_stream_pair(const SkinnyArgs& a, const Levels& lv, const W4Pla
     WQ_PAIR(63, 8, 4, 1, 16, 2)
     WQ_PAIR(64, 8, 6, 1, 16, 2)
     WQ_PAIR(65, 8, 8, 1, 16, 2)
+    WQ_PAIR(67, 8, 6, 1, 16, 1)
     default: return hipErrorInvalidConfiguration;
   }
 #undef WQ_PAIR
@@ -1312,7 +1313,7 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
   struct PCfg { int id, nw, tpg, gpp, mp, nbuf; };
   static const PCfg pcfgs[] = {{60, 8, 2, 1, 1, 2},  {61, 8, 2, 1, 4, 2}, {62, 8, 2, 1, 16, 2},
                                {63, 8, 4, 1, 16, 2}, {64, 8, 6, 1, 16, 2},
-                               {65, 8, 8, 1, 16, 2}};
+                               {65, 8, 8, 1, 16, 2}, {67, 8, 6, 1, 16, 1}};
   W4Plan p = plan_w4a16(m, wg);
   p.szl = p.szl && plan_w4a16(m, wu).szl;
   if (p.path == 1) return p;
@@ -1324,8 +1325,12 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
   } else if (m <= 4) {
     cfg = 61;
   } else {
+    // three row tiles of each matrix (the 11008-row gate/up shape): one
+    // phase in flight per wave measured faster than two (15.2-15.6 against
+    // 16.3-16.8 us for the pair at m = 16, A/B on one box, twice); the
+    // twelve code loads of a phase already keep the CU busy
     const int64_t th = (ntiles + 255) / 256;
-    cfg = th >= 4 ? 65 : th == 3 ? 64 : (th == 2 ? 63 : 62);
+    cfg = th >= 4 ? 65 : th == 3 ? 67 : (th == 2 ? 63 : 62);
   }
 #ifdef WQ_TUNE_ENV
   if (const char* e = getenv("WQ_PAIR")) {

@@ -163,6 +163,7 @@ def test_linear_gemm_parity(m, n, k, xdt, ydt):
     (9, 1000, 2048, "f16", "bf16"),   # one row tile per matrix, 16 staged rows
     (16, 5120, 4096, "f16", "f32"),   # two row tiles per matrix
     (16, 11008, 4096, "f16", "f16"),  # the full gate/up shape: three row tiles per matrix
+    (12, 11008, 2048, "bf16", "f32"), # three row tiles per matrix, bf16 (exact decoder)
     (16, 14336, 4096, "f16", "f32"),  # four row tiles per matrix
     (1, 4096, 11008, "f16", "f32"),   # 86 groups
     (40, 520, 1024, "f16", "f32"),    # prefill rows: two GEMMs
@@ -243,7 +244,8 @@ def test_linear_group_sizes(m, n, k, xdt, ydt, group):
     say(f"  max-rel {rel:.2e}")
 
 
-@pytest.mark.parametrize("m,n,k,group,act", [(16, 5120, 4096, 64, 0), (1, 300, 1152, 32, 1)])
+@pytest.mark.parametrize("m,n,k,group,act", [(16, 5120, 4096, 64, 0), (1, 300, 1152, 32, 1),
+                                             (16, 11008, 2048, 32, 1)])
 def test_gate_up_group_sizes(m, n, k, group, act):
     say(f"gate_up_group m={m} n={n} k={k} group={group} act={act}")
     seed = 700 + m + n

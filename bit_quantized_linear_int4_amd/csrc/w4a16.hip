@@ -1091,6 +1091,7 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
     WQ_STR(50, 8, 2, 1, 16, 2)
     WQ_STR(51, 8, 4, 1, 16, 2)
     WQ_STR(54, 8, 2, 1, 4, 2)
+    WQ_STR(74, 16, 1, 1, 1, 2)
     default: return hipErrorInvalidConfiguration;
   }
 #undef WQ_STR
@@ -1227,7 +1228,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
       {22, 8, 1, 1, 1, 4},  {27, 8, 3, 1, 16, 4},  {40, 8, 1, 1, 1, 2},  {41, 8, 1, 1, 1, 3},
       {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2},  {44, 8, 3, 1, 16, 3},  {45, 8, 1, 1, 16, 2},
       {46, 8, 1, 1, 16, 3},  {47, 8, 1, 2, 1, 2},  {50, 8, 2, 1, 16, 2},  {51, 8, 4, 1, 16, 2},
-      {54, 8, 2, 1, 4, 2}};
+      {54, 8, 2, 1, 4, 2},  {74, 16, 1, 1, 1, 2}};
   W4Plan p;
   p.path = m > 16 ? 1 : 3;
   p.tpg = 1;
@@ -1252,12 +1253,15 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   // wave's loads complete in issue order, so its multiply waits for all of
   // them.
   //  m = 1: eight waves, one group per wave and phase (two for long K);
+  //         sixteen waves for INT4 with at most one workgroup per CU and
+  //         K below 64 groups (4096x4096: 5.02 against 5.19 us per call,
+  //         A/B on one box, twice; NF4 and larger grids measured slower);
   //  m <= 4: eight waves, one tile;
   //  m <= 16: one workgroup per CU, as many tiles per workgroup as that
   //           takes (at most 4; more tiles take several rounds).
   int cfg;
   if (m <= 1) {
-    cfg = G >= 64 ? 47 : 40;
+    cfg = G >= 64 ? 47 : (w->fmt == WQ_FMT_INT4_ASYM && ntiles <= 256 ? 74 : 40);
   } else if (m <= 4) {
     cfg = 42;
   } else {

@@ -1,13 +1,17 @@
 """Benchmark of the quantized linear path on one MI355X.
 
-Default workload: the 7B-style MLP decode batch -- M = 16 tokens through
-gate [11008 x 4096], up [11008 x 4096] and down [4096 x 11008] INT4 layers
-(group 128, fp16 scale, 4-bit zero point), fp16 activations, fp16 outputs.
-One step is the three dequant-GEMV calls.  Weights are quantized on the GPU
-once (offline step, outside the timed region) and replicated into enough
-distinct copies (>= 512 MB) that successive steps read weights the 256 MB
-Infinity Cache has not just served; inputs are resident in HBM when timing
-starts.
+Default (--workload metric): the two shapes the metric is quoted on, in one
+JSON line.
+  * value: the single W4A16 layer at M = 1 -- W [4096 x 4096] INT4 (group
+    128, fp16 scale, 4-bit zero point), x fp16 [1 x 4096], y fp16; one step
+    is one dequant-GEMV call; effective HBM GB/s.
+  * secondary: the 7B-style prefill at M = 2048 -- q, k, v, o [4096 x 4096]
+    and up [11008 x 4096], one step is the five dequant-GEMM calls; TFLOP/s.
+Each carries the roofline of its dominant kernel.  Weights are quantized on
+the GPU once (offline step, outside the timed region) and replicated into
+enough distinct copies (>= 512 MB) that successive steps read weights the
+256 MB Infinity Cache has not just served; inputs are resident in HBM when
+timing starts.
 
 Timing.  The K timed steps are captured into one HIP graph and replayed
 once between two HIP events on the capture stream (warmup: W eager steps,
@@ -20,9 +24,10 @@ Reported value: effective HBM GB/s = algorithmic bytes of one step (packed
 codes + scales + zero points + x + y, each read or written once) / step time
 (TFLOP/s = 2*M*N*K / step time for the GEMM workloads).
 
-Other workloads (--workload): decode_m1 (M = 1, 4096 x 4096), prefill
-(M = 2048 through q, k, v, o and up), nf4_m1 / nf4_m512 (NF4 14336 x 4096,
-bf16), int8_70b (LLM.int8 at 28672 x 8192, M = 256).
+Other workloads (--workload), one per line: decode_m1, prefill, mlp_decode
+(M = 16 through gate + up as one pair call and down [4096 x 11008]),
+nf4_m1 / nf4_m512 (NF4 14336 x 4096, bf16), int8_70b (LLM.int8 at
+28672 x 8192, M = 256).
 """
 
 import argparse
@@ -70,7 +75,7 @@ class Workload:
         self.unit = unit
 
     # to be provided: setup(), step_calls(copy), dominant_calls(copy),
-    # work_per_step(), dominant_work(), cpu_sample(), config()
+    # work_per_step(), dominant_work(), cpu_stages(), config(), release()
 
 
 def _int4_weight(wq, torch, w_np):
@@ -161,29 +166,33 @@ class W4Layers(Workload):
         per = self.ubytes if self.unit == "GB/s" else self.uflops
         return per[self.dom[0]]
 
-    def cpu_sample(self):
-        """Oracle: quantize, dequantize and fp64 product on the first rows of
-        every layer."""
+    def cpu_stages(self):
+        """The oracle's stages on the first layer (its first 4096 rows):
+        quantize + pack, dequantize, fp64 reference product."""
         import numpy as np
         from oracle import int4, linear
-        frac = 32 if self.unit == "GB/s" else 256
-        sample = [(nm, x, w[:max(16, w.shape[0] // frac)]) for nm, x, w in self.layers_np]
+        nm, x, w = self.layers_np[0]
+        w = w[:4096]
+        m, n, k = x.shape[0], w.shape[0], w.shape[1]
+        st = {}
 
-        def run():
-            for _, x, w in sample:
-                q, s, z = int4.quantize(w)
-                wh = int4.dequantize(q, s, z, w.shape[1])
-                linear.reference(x.astype(np.float32), wh)
-        work = 0
-        for _, x, w in sample:
-            m, n, k = x.shape[0], w.shape[0], w.shape[1]
-            if self.unit == "GB/s":
-                g = k // 128
-                work += n * k // 2 + n * g * 2 + n * ((g + 1) // 2) + x.size * 2 + m * n * 2
-            else:
-                work += 2 * m * n * k
-        desc = ", ".join(f"{nm} first {w.shape[0]} rows" for nm, _, w in sample)
-        return run, work, desc + "; oracle quantize + dequantize + fp64 product"
+        def quant():
+            st["q"] = int4.quantize(w)
+
+        def deq():
+            st["wh"] = int4.dequantize(*st["q"], k)
+
+        def ref():
+            linear.reference(x.astype(np.float32), st["wh"])
+        g = k // 128
+        work = (n * k // 2 + n * g * 2 + n * ((g + 1) // 2) + m * k * 2 + m * n * 2
+                if self.unit == "GB/s" else 2 * m * n * k)
+        desc = f"{nm} layer, rows 0..{n - 1} of {self.layers_np[0][2].shape[0]}, M={m}, K={k}"
+        return [("quantize_pack", quant), ("dequantize", deq), ("reference_linear_fp64", ref)], \
+            work, desc
+
+    def release(self):
+        self.copies = self.xs = self.ys = self.wss = None
 
     def config(self):
         return {"workload": self.name,
@@ -229,22 +238,31 @@ class NF4Layer(Workload):
 
     dominant_work = work_per_step
 
-    def cpu_sample(self):
+    def cpu_stages(self):
         import numpy as np
         from oracle import nf4, linear, numerics
         (_, x, w), = self.layers_np
-        rows = max(64, w.shape[0] // (64 if self.unit == "GB/s" else 512))
+        rows = 4096 if self.unit == "GB/s" else 1024
         ws = numerics.bf16_bits_to_f32(w[:rows])
         xs = numerics.bf16_bits_to_f32(x)
+        st = {}
 
-        def run():
-            c, a, c2 = nf4.quantize(ws, double_quant=True)
-            wh = nf4.dequantize(c, a, c2, ws.shape, out_dtype="bf16")
-            linear.reference(xs, wh)
+        def quant():
+            st["q"] = nf4.quantize(ws, double_quant=True)
+
+        def deq():
+            st["wh"] = nf4.dequantize(*st["q"], ws.shape, out_dtype="bf16")
+
+        def ref():
+            linear.reference(xs, st["wh"])
         m, k = x.shape
         work = (rows * k // 2 + rows * k // 64 + m * k * 2 + m * rows * 2
                 if self.unit == "GB/s" else 2 * m * rows * k)
-        return run, work, f"first {rows} rows; oracle NF4 quantize + dequantize + fp64 product"
+        return [("quantize_pack", quant), ("dequantize", deq), ("reference_linear_fp64", ref)], \
+            work, f"rows 0..{rows - 1} of {w.shape[0]}, M={m}, K={k}"
+
+    def release(self):
+        self.copies = self.x = self.y = None
 
     def config(self):
         (_, x, w), = self.layers_np
@@ -287,18 +305,25 @@ class Int8Layer(Workload):
 
     dominant_work = work_per_step
 
-    def cpu_sample(self):
+    def cpu_stages(self):
         from oracle import llm_int8
         (_, x, w), = self.layers_np
-        rows = 512
+        rows = 1024
         wsub = w[:rows]
+        st = {}
 
-        def run():
-            qw, sw = llm_int8.quantize_rows(wsub)
-            llm_int8.linear(x, qw, sw, 6.0)
+        def quant():
+            st["q"] = llm_int8.quantize_rows(wsub)
+
+        def lin():
+            llm_int8.linear(x, *st["q"], 6.0)
         m, k = x.shape
         work = rows * k + rows * 4 + m * k * 2 + m * rows * 2
-        return run, work, f"first {rows} rows; oracle LLM.int8 quantize + decomposition"
+        return [("quantize_rows", quant), ("decomposition_fp64", lin)], \
+            work, f"rows 0..{rows - 1} of {w.shape[0]}, M={m}, K={k}"
+
+    def release(self):
+        self.copies = self.x = self.y = self.ws = None
 
     def config(self):
         (_, x, w), = self.layers_np
@@ -379,6 +404,8 @@ def traffic_from_profile(wl):
 
 
 def cpu_threads():
+    """Threads for the all-cores setting: the cores this process may run on,
+    at most 16 (the host CPU share of one GPU on the measurement boxes)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
@@ -386,22 +413,75 @@ def cpu_threads():
     return max(1, min(n, 16))
 
 
-def cpu_baseline(wl, budget_s):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def oracle_stage_times(wl, threads, reps=3):
+    """Median wall time of each oracle stage at `threads` BLAS/OpenMP threads."""
+    import statistics
     import threadpoolctl
-    cores = cpu_threads()
-    run, work, desc = wl.cpu_sample()
-    reps, t = 0, 0.0
-    with threadpoolctl.threadpool_limits(limits=cores):
-        t0 = time.perf_counter()
-        while True:
-            run()
-            reps += 1
-            t = time.perf_counter() - t0
-            if t > budget_s or reps >= 100:
-                break
-    scale = 1e9 if wl.unit == "GB/s" else 1e12
-    return {"value": round(work * reps / t / scale, 6), "unit": wl.unit, "cores": cores,
-            "kind": "oracle", "sample": f"{desc}; {reps} repetitions in {t:.1f} s"}
+    stages, work, desc = wl.cpu_stages()
+    med = {}
+    with threadpoolctl.threadpool_limits(limits=threads):
+        for _ in range(reps):
+            for name, fn in stages:
+                t0 = time.perf_counter()
+                fn()
+                med.setdefault(name, []).append(time.perf_counter() - t0)
+    med = {k: statistics.median(v) for k, v in med.items()}
+    return med, work, desc
+
+
+def cpu_baseline(wls):
+    """The oracle (as it stands) on the host cores: every stage of the first
+    workload timed at 1 thread and at all threads (median of 3), the whole
+    path's rate on the sample as `value`; the same for the secondary
+    workload."""
+    allc = cpu_threads()
+    out = {}
+    for i, wl in enumerate(wls):
+        one, work, desc = oracle_stage_times(wl, 1)
+        many, _, _ = oracle_stage_times(wl, allc)
+        scale = 1e9 if wl.unit == "GB/s" else 1e12
+        rec = {"value": round(work / sum(many.values()) / scale, 6), "unit": wl.unit,
+               "cores": allc, "kind": "oracle",
+               "sample": f"{wl.name}: {desc}; every stage once per repetition, median of 3",
+               "value_1_thread": round(work / sum(one.values()) / scale, 6),
+               "stages_s_1_thread": {k: round(v, 4) for k, v in one.items()},
+               f"stages_s_{allc}_threads": {k: round(v, 4) for k, v in many.items()}}
+        if i == 0:
+            out.update(rec)
+            out.update({"nproc": os.cpu_count(), "cpu_model": cpu_model(),
+                        "threads_note": "NumPy elementwise stages run on one thread in both "
+                                        "settings; only the fp64 BLAS product uses more"})
+        else:
+            out["secondary"] = rec
+    return out
+
+
+# The pages' own figures, all on NVIDIA GPUs and all end-to-end model numbers
+# (no page gives a kernel-level figure for this path): context only.
+PAGES_CONTEXT = [
+    {"figure": "LLM.int8 generation speed relative to FP16", "value": "about 1.05-1.1x",
+     "hardware": "A100 80G", "workload": "13B model",
+     "page": "LLM quantization selection: five mainstream schemes compared, section 2.2"},
+    {"figure": "4-bit weights of a 7B model", "value": "about 3.5 GB (14 GB in FP16)",
+     "page": "the quantization-concepts article, opening"},
+    {"figure": "LLaMA-2-7B decode throughput", "value":
+     "FP16 95 tok/s, GPTQ-4bit 110, AWQ-4bit 125, bitsandbytes NF4 70",
+     "hardware": "A100 80G",
+     "page": "Inference & deployment 05: quantized deployment compared, section 9.2"},
+    {"figure": "group size 32 against 128", "value": "about 8% slower generation",
+     "hardware": "RTX 3060", "workload": "7B, 4-bit",
+     "page": "Open-source model quantization guide: GGUF, GPTQ, AWQ, section 4.3"},
+]
 
 
 def copy_probe(mib):
@@ -545,6 +625,36 @@ def summarize_trace(prof_dir, bench_json, title, out_path, command):
     print(open(out_path).read())
 
 
+def measure(wl, steps, warmup):
+    """Graph-replayed step time and the dominant kernel's average launch
+    time of a set-up workload, as the bench line's value / roofline fields."""
+    log(f"[bench] timing {steps} steps of {wl.name} after {warmup} warmup")
+    ms = timed_graph(wl.step_calls, steps, warmup)
+    ms_step = ms / steps
+    log(f"[bench] timing the dominant kernel: {wl.kernel_desc}")
+    ndom = len(wl.dominant_calls(0))
+    ms_dom = timed_graph(wl.dominant_calls, steps, 2)
+    launches = steps * ndom
+    us_launch = ms_dom * 1e3 / launches
+    scale = 1e9 if wl.unit == "GB/s" else 1e12
+    value = wl.work_per_step() / (ms_step * 1e-3) / scale
+    achieved = wl.dominant_work() / (us_launch * 1e-6) / scale
+    bound = "hbm" if wl.unit == "GB/s" else "mfma"
+    peak = HBM_PEAK_GBS if bound == "hbm" else MFMA16_PEAK_TFLOPS
+    return {
+        "value": round(value, 3),
+        "unit": wl.unit,
+        "ms_per_step": round(ms_step, 5),
+        "dtype": wl.dtype,
+        "config": wl.config(),
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
+                     "unit": wl.unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic_from_profile(wl),
+                     "kernel": wl.kernel_desc, "avg_launch_us": round(us_launch, 3),
+                     "work_per_launch": wl.dominant_work(), "launches": launches},
+    }
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         # --summarize-trace PROF_DIR BENCH_JSON TITLE OUT "COMMAND"
@@ -565,11 +675,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mlp_decode",
-                    choices=["mlp_decode", "decode_m1", "prefill", "nf4_m1", "nf4_m512",
-                             "int8_70b"])
+    ap.add_argument("--workload", default="metric",
+                    choices=["metric", "mlp_decode", "decode_m1", "prefill", "nf4_m1", "nf4_m512",
+                             "int8_70b"],
+                    help="metric (default): the M = 1 decode layer as the value, with the "
+                         "M = 2048 prefill step as the secondary figure in the same line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB five times (the reference "
                          "dispatch for scaling rocprofv3 byte counters)")
@@ -582,46 +693,43 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args.copy_probe)
-    wl = make_workload(args.workload)
-    log(f"[bench] setting up {wl.name}")
-    wl.setup()
-    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
-    ms = timed_graph(wl.step_calls, args.steps, args.warmup)
-    ms_step = ms / args.steps
-    log(f"[bench] timing the dominant kernel: {wl.kernel_desc}")
-    ndom = len(wl.dominant_calls(0))
-    ms_dom = timed_graph(wl.dominant_calls, args.steps, 2)
-    launches = args.steps * ndom
-    us_launch = ms_dom * 1e3 / launches
-    scale = 1e9 if wl.unit == "GB/s" else 1e12
-    value = wl.work_per_step() / (ms_step * 1e-3) / scale
-    achieved = wl.dominant_work() / (us_launch * 1e-6) / scale
-    bound = "hbm" if wl.unit == "GB/s" else "mfma"
-    peak = HBM_PEAK_GBS if bound == "hbm" else MFMA16_PEAK_TFLOPS
+    names = ["decode_m1", "prefill"] if args.workload == "metric" else [args.workload]
+    results, wls = [], []
+    for name in names:
+        wl = make_workload(name)
+        log(f"[bench] setting up {wl.name}")
+        wl.setup()
+        results.append(measure(wl, args.steps, args.warmup))
+        wls.append(wl)
+        wl.release()
+        torch.cuda.empty_cache()
+    head = results[0]
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": wl.unit,
+        "value": head["value"],
+        "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic: seeded N(0,0.02) weights, N(0,1) activations with fixed outlier "
-                "channels (decode), random-init layers of the 7B/8B/70B shapes",
-        "config": wl.config(),
-        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
-                     "unit": wl.unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic_from_profile(wl),
-                     "kernel": wl.kernel_desc, "avg_launch_us": round(us_launch, 3),
-                     "work_per_launch": wl.dominant_work(), "launches": launches},
+        "dtype": head["dtype"],
+        "data": "synthetic: seeded N(0,0.02) weights, N(0,1) activations (fixed outlier "
+                "channels where the workload has them), random-init layers of the 7B/8B/70B "
+                "shapes",
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
+    if len(results) > 1:
+        sec = dict(results[1])
+        sec["metric"] = "W4A16 g128 prefill dequant-GEMM TFLOP/s (M=2048)"
+        out["secondary"] = sec
+    out["context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle sample")
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(wls)
     print(json.dumps(out), flush=True)
 
 

@@ -128,6 +128,93 @@ def _stream(stream, t):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+# ------------------------------------------------------------ validation
+# Sizes and layouts are checked here, before the C call: the C layer sees
+# only pointers and the sizes passed to it, so a tensor smaller than the
+# sizes say would be read or written out of bounds on the device.  Shape and
+# layout mismatches raise WqError(WQ_ERR_SHAPE); tensors that are not GPU
+# tensors raise WqError(WQ_ERR_UNSUPPORTED).
+_ERR_SHAPE, _ERR_UNSUP = 2, 4
+
+
+def _fail(what, msg, status=_ERR_SHAPE):
+    raise WqError(status, f"{what}: {msg}")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _dense(what, name, t, nbytes=None, shape=None):
+    """`t` is contiguous, with `shape` (if given) and exactly `nbytes` bytes
+    (if given)."""
+    if t is None:
+        _fail(what, f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        _fail(what, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        _fail(what, f"{name} is not contiguous")
+    if nbytes is not None and _nbytes(t) != nbytes:
+        _fail(what, f"{name} holds {_nbytes(t)} bytes, expected {nbytes}")
+
+
+def _on_gpu(what, *ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            _fail(what, "tensors must be GPU tensors", _ERR_UNSUP)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            _fail(what, "tensors are on different devices", _ERR_UNSUP)
+
+
+def _matrix(what, name, t):
+    if t is None or t.dim() != 2:
+        _fail(what, f"{name} must be a 2-D [rows][k] tensor")
+    _dense(what, name, t)
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _weight_tensors(what, w):
+    """The tensors of a QuantizedWeight against the sizes its descriptor
+    states (layouts as in wq_weight)."""
+    n, k, g = w.n, w.k, w.group
+    if n < 1 or k < 1 or g < 1 or k % 8:
+        _fail(what, f"weight sizes n={n} k={k} group={g} are invalid")
+    if w.fmt == FMT_INT4_ASYM:
+        if k % g:
+            _fail(what, f"k={k} is not a multiple of the group {g}")
+        ng = k // g
+        _dense(what, "codes", w.codes, n * k // 2)
+        _dense(what, "scales", w.scales, 2 * n * ng)
+        _dense(what, "zeros", w.zeros, n * ((ng + 1) // 2))
+        if w.perm is not None:
+            _dense(what, "perm", w.perm, 4 * k)
+    elif w.fmt in (FMT_NF4, FMT_FP4):
+        if (n * k) % g:
+            _fail(what, f"n*k={n * k} is not a multiple of the block {g}")
+        nb = n * k // g
+        _dense(what, "codes", w.codes, n * k // 2)
+        if w.scales2 is not None:
+            if w.group2 < 1:
+                _fail(what, f"group2={w.group2} is invalid")
+            _dense(what, "absmax", w.scales, nb)
+            _dense(what, "absmax_scale", w.scales2, 4 * (-(-nb // w.group2)))
+        else:
+            _dense(what, "absmax", w.scales, 4 * nb)
+        if w.perm is not None:
+            _dense(what, "perm", w.perm, 4 * k)
+    elif w.fmt == FMT_INT8_SYM_ROW:
+        _dense(what, "codes", w.codes, n * k)
+        _dense(what, "scales", w.scales, 4 * n)
+    else:
+        _fail(what, f"unknown weight format {w.fmt}", _ERR_UNSUP)
+    return [w.codes, w.scales, w.zeros, w.scales2, w.perm]
+
+
 class QuantizedWeight:
     """Device tensors of one quantized weight plus its wq_weight descriptor."""
 
@@ -196,21 +283,56 @@ def alloc_int8(n, k, device="cuda"):
 
 
 def wq_quantize_groupwise(w, bits, group, symmetric, codes, scales, zeros=None, stream=None):
-    n, k = w.shape
+    what = "wq_quantize_groupwise"
+    n, k = _matrix(what, "w", w)
+    if bits == 4:
+        if group < 1 or k % group:
+            _fail(what, f"k={k} is not a multiple of the group {group}")
+        ng = k // group
+        _dense(what, "codes", codes, n * k // 2)
+        _dense(what, "scales", scales, 2 * n * ng)
+        _dense(what, "zeros", zeros, n * ((ng + 1) // 2))
+    elif bits == 8:
+        _dense(what, "codes", codes, n * k)
+        _dense(what, "scales", scales, 4 * n)
+        if zeros is not None:
+            _fail(what, "zeros must be None for 8-bit symmetric codes", _ERR_UNSUP)
+    else:
+        _fail(what, f"bits={bits} group={group} do not fit k={k}", _ERR_UNSUP)
+    _on_gpu(what, w, codes, scales, zeros)
     st = _load().wq_quantize_groupwise(_ptr(w), _dt(w), n, k, bits, group, symmetric,
                                        _ptr(codes), _ptr(scales), _ptr(zeros), _stream(stream, w))
     _check(st, "wq_quantize_groupwise")
 
 
+def _check_pack(what, w, block, double_quant, block2, codes, absmax, absmax_scale):
+    n, k = _matrix(what, "w", w)
+    if block < 1 or (n * k) % block or (double_quant and block2 < 1):
+        _fail(what, f"block={block} block2={block2} do not fit n*k={n * k}")
+    nb = n * k // block
+    _dense(what, "codes", codes, n * k // 2)
+    if double_quant:
+        _dense(what, "absmax", absmax, nb)
+        _dense(what, "absmax_scale", absmax_scale, 4 * (-(-nb // block2)))
+    else:
+        _dense(what, "absmax", absmax, 4 * nb)
+        if absmax_scale is not None:
+            _fail(what, "absmax_scale must be None without double quantization", _ERR_UNSUP)
+    _on_gpu(what, w, codes, absmax, absmax_scale)
+    return n, k
+
+
 def wq_pack_nf4(w, block, double_quant, block2, codes, absmax, absmax_scale=None, stream=None):
-    n, k = w.shape
+    n, k = _check_pack("wq_pack_nf4", w, block, double_quant, block2, codes, absmax,
+                       absmax_scale)
     st = _load().wq_pack_nf4(_ptr(w), _dt(w), n, k, block, 1 if double_quant else 0, block2,
                              _ptr(codes), _ptr(absmax), _ptr(absmax_scale), _stream(stream, w))
     _check(st, "wq_pack_nf4")
 
 
 def wq_pack_fp4(w, block, double_quant, block2, codes, absmax, absmax_scale=None, stream=None):
-    n, k = w.shape
+    n, k = _check_pack("wq_pack_fp4", w, block, double_quant, block2, codes, absmax,
+                       absmax_scale)
     st = _load().wq_pack_fp4(_ptr(w), _dt(w), n, k, block, 1 if double_quant else 0, block2,
                              _ptr(codes), _ptr(absmax), _ptr(absmax_scale), _stream(stream, w))
     _check(st, "wq_pack_fp4")
@@ -233,7 +355,22 @@ def wq_linear_w4a16_workspace(m, weight):
     return int(_load().wq_linear_w4a16_workspace(int(m), ctypes.byref(d)))
 
 
+def _check_linear(what, x, weight, ys):
+    m, k = _matrix(what, "x", x)
+    if k != weight.k:
+        _fail(what, f"x has k={k}, the weight k={weight.k}")
+    wt = _weight_tensors(what, weight)
+    for name, y in ys:
+        _dense(what, name, y, shape=(m, weight.n))
+    return m, [x] + wt + [y for _, y in ys]
+
+
 def wq_linear_w4a16(x, weight, y, workspace=None, stream=None):
+    what = "wq_linear_w4a16"
+    _, ts = _check_linear(what, x, weight, [("y", y)])
+    if workspace is not None:
+        _dense(what, "workspace", workspace)
+    _on_gpu(what, workspace, *ts)
     d = weight.descriptor()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _load().wq_linear_w4a16(_ptr(x), _dt(x), x.shape[0], ctypes.byref(d), _ptr(y), _dt(y),
@@ -242,6 +379,11 @@ def wq_linear_w4a16(x, weight, y, workspace=None, stream=None):
 
 
 def wq_linear_w4a16_gate_up(x, w_gate, w_up, y_gate, y_up=None, act=0, stream=None):
+    what = "wq_linear_w4a16_gate_up"
+    _, tg = _check_linear(what, x, w_gate,
+                          [("y_gate", y_gate)] + ([("y_up", y_up)] if act == 0 else []))
+    _, tu = _check_linear(what, x, w_up, [])
+    _on_gpu(what, *tg, *tu)
     dg, du = w_gate.descriptor(), w_up.descriptor()
     st = _load().wq_linear_w4a16_gate_up(_ptr(x), _dt(x), x.shape[0], ctypes.byref(dg),
                                          ctypes.byref(du), int(act), _ptr(y_gate), _ptr(y_up),
@@ -250,7 +392,14 @@ def wq_linear_w4a16_gate_up(x, w_gate, w_up, y_gate, y_up=None, act=0, stream=No
 
 
 def wq_int8_prepare_activations(x, threshold, mask, idx, count, qx, sx, stream=None):
-    m, k = x.shape
+    what = "wq_int8_prepare_activations"
+    m, k = _matrix(what, "x", x)
+    _dense(what, "mask", mask, k)
+    _dense(what, "idx", idx, 4 * k)
+    _dense(what, "count", count, 4)
+    _dense(what, "qx", qx, m * k)
+    _dense(what, "sx", sx, 4 * m)
+    _on_gpu(what, x, mask, idx, count, qx, sx)
     st = _load().wq_int8_prepare_activations(_ptr(x), m, k, float(threshold), _ptr(mask),
                                              _ptr(idx), _ptr(count), _ptr(qx), _ptr(sx),
                                              _stream(stream, x))
@@ -263,6 +412,14 @@ def wq_linear_int8_decomp_workspace(m, k):
 
 def wq_linear_int8_decomp(x, weight, threshold, y, workspace, outlier_count=None, acc_out=None,
                           stream=None):
+    what = "wq_linear_int8_decomp"
+    m, ts = _check_linear(what, x, weight, [("y", y)])
+    _dense(what, "workspace", workspace)
+    if outlier_count is not None:
+        _dense(what, "outlier_count", outlier_count, 4)
+    if acc_out is not None:
+        _dense(what, "acc_out", acc_out, 4 * m * weight.n)
+    _on_gpu(what, workspace, outlier_count, acc_out, *ts)
     d = weight.descriptor()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _load().wq_linear_int8_decomp(_ptr(x), x.shape[0], ctypes.byref(d), float(threshold),
@@ -272,20 +429,32 @@ def wq_linear_int8_decomp(x, weight, threshold, y, workspace, outlier_count=None
 
 
 def wq_permute_columns(src, perm, dst, stream=None):
-    rows, k = src.shape
+    what = "wq_permute_columns"
+    rows, k = _matrix(what, "src", src)
+    _dense(what, "perm", perm, 4 * k)
+    _dense(what, "dst", dst, _nbytes(src), shape=(rows, k))
+    _on_gpu(what, src, perm, dst)
     st = _load().wq_permute_columns(_ptr(src), _dt(src), rows, k, _ptr(perm), _ptr(dst),
                                     _stream(stream, src))
     _check(st, "wq_permute_columns")
 
 
 def wq_scale_columns(src, scale, dst, stream=None):
-    rows, k = src.shape
+    what = "wq_scale_columns"
+    rows, k = _matrix(what, "src", src)
+    _dense(what, "scale", scale, 4 * k)
+    _dense(what, "dst", dst, _nbytes(src), shape=(rows, k))
+    _on_gpu(what, src, scale, dst)
     st = _load().wq_scale_columns(_ptr(src), _dt(src), rows, k, _ptr(scale), _ptr(dst),
                                   _stream(stream, src))
     _check(st, "wq_scale_columns")
 
 
 def wq_dequantize(weight, out, stream=None):
+    what = "wq_dequantize"
+    wt = _weight_tensors(what, weight)
+    _dense(what, "out", out, shape=(weight.n, weight.k))
+    _on_gpu(what, out, *wt)
     d = weight.descriptor()
     st = _load().wq_dequantize(ctypes.byref(d), _ptr(out), _dt(out), _stream(stream, out))
     _check(st, "wq_dequantize")

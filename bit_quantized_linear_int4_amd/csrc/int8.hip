@@ -414,10 +414,13 @@ __global__ __launch_bounds__(256) void int8_gemm_kernel(Int8GemmArgs a) {
       for (int j = 0; j < NT; ++j) {
         const int nn = n0 + j * 16 + nl;
         if (mm < a.m && nn < a.n) {
+          const int64_t o = (int64_t)mm * a.n + nn;
           if constexpr (YDT == WQ_F32)
-            static_cast<float*>(a.y)[(int64_t)mm * a.n + nn] = yf[i][j][e];
+            static_cast<float*>(a.y)[o] = yf[i][j][e];
+          else if constexpr (YDT == WQ_BF16)
+            static_cast<uint16_t*>(a.y)[o] = f32_to_bf16_bits(yf[i][j][e]);
           else
-            static_cast<uint16_t*>(a.y)[(int64_t)mm * a.n + nn] = f32_to_f16_bits(yf[i][j][e]);
+            static_cast<uint16_t*>(a.y)[o] = f32_to_f16_bits(yf[i][j][e]);
         }
       }
     }
@@ -428,6 +431,8 @@ hipError_t launch_int8_gemm_nt(const Int8GemmArgs& a, int ydt, hipStream_t s) {
   const dim3 grid((unsigned)((a.n + NT * 16 - 1) / (NT * 16)), (unsigned)((a.m + kI8BM - 1) / kI8BM));
   if (ydt == WQ_F32)
     int8_gemm_kernel<NT, WQ_F32><<<grid, 256, 0, s>>>(a);
+  else if (ydt == WQ_BF16)
+    int8_gemm_kernel<NT, WQ_BF16><<<grid, 256, 0, s>>>(a);
   else
     int8_gemm_kernel<NT, WQ_F16><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();

@@ -48,8 +48,6 @@
 //    into LDS in the activation type, four waves of 64 x 64.
 #include <algorithm>
 #include <atomic>
-#include <cstdio>
-#include <cstdlib>
 #include <type_traits>
 #include <utility>
 
@@ -128,7 +126,6 @@ struct SkinnyArgs {
   const float* scales2;      // NF4 double-quant second level, or nullptr
   int m, n, k, G, zb;        // G = k/128 units of 128; zb = bytes per row of zeros
   int GS, sub;               // INT4: groups per row (k/group), groups per unit (1, 2, 4)
-  float* partial;            // [splits][m][n] when the K range is split
   void* y;
   // second INT4 matrix of a gate/up pair (same n, k; same x), its output,
   // and the epilogue: 0 = both outputs, 1 = y = silu(gate) * up only
@@ -235,8 +232,7 @@ __device__ __forceinline__ void vm_wait_n(int n) { vm_wait_range<0, 63>(n); }
 // registers.
 template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF, bool SZL,
           bool DUAL, bool SG>
-__global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv, int phases,
-                                                         int kslice) {
+__global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv, int phases) {
   // DUAL: TPG counts the tiles of both matrices; tile t < TH is row tile t
   // of the first (gate) matrix, tile TH + t the same rows of the second (up)
   constexpr int TH = DUAL ? TPG / 2 : TPG;                 // row tiles per workgroup
@@ -263,9 +259,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // each unit of 128, i.e. group unit * sub + lq
   const int lq = (kq * a.sub) >> 2;
   const int ntiles = (a.n + 15) / 16;
-  // this workgroup's K slice: units [gbeg, gend)
-  const int gbeg = (int)blockIdx.y * kslice;
-  const int gend = min(a.G, gbeg + kslice);
+  // every workgroup covers the whole K range: units [0, G)
+  constexpr int gbeg = 0;
+  const int gend = a.G;
   uint4_t* const ring = dsm + wave * NBUF * XS;
   // staged scales / zeros: per tile SCB and ZCB bytes (multiples of 1 KB)
   const int SCB = (32 * a.GS + 1023) / 1024 * 1024;
@@ -555,23 +551,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
         }
         continue;
       }
-      if (gridDim.y > 1)
-        a.partial[((int64_t)blockIdx.y * a.m + mm) * a.n + nn] = v;
-      else
-        store_y<YDT>(a.y, (int64_t)mm * a.n + nn, v);
+      store_y<YDT>(a.y, (int64_t)mm * a.n + nn, v);
     }
   }
-}
-
-// Sum of the K-slice partial results in a fixed order (deterministic).
-template <int YDT>
-__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int splits,
-                                                         int64_t mn, void* y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= mn) return;
-  float v = part[i];
-  for (int s = 1; s < splits; ++s) v += part[(int64_t)s * mn + i];
-  store_y<YDT>(y, i, v);
 }
 
 // Dynamic LDS bytes of one stream_kernel workgroup.
@@ -763,10 +745,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
 //    are staged into LDS once.
 // Staged scale / zero-point capacity: 256 rows x up to kGemmMaxGroups groups.
 constexpr int kGemmMaxGroups = 64;
-#ifndef WQ_GEMM_WAVES
-#define WQ_GEMM_WAVES 8
-#endif
-constexpr int kGemmWaves = WQ_GEMM_WAVES;   // 4: 128 x 64 per wave; 8: 128 x 32
+constexpr int kGemmWaves = 8;   // 128 x 32 per wave, two waves per SIMD
 constexpr int kGemmScaleBytes = 256 * kGemmMaxGroups * 2;
 constexpr int kGemmZeroBytes = 256 * kGemmMaxGroups / 2;
 
@@ -1048,13 +1027,7 @@ hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& 
     while (lds > cur && !allowed.compare_exchange_weak(cur, lds)) {
     }
   }
-  kern<<<dim3((unsigned)p.grid, (unsigned)p.splits), NW * 64, lds, s>>>(a, lv, p.phases,
-                                                                         p.kslice);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t mn = (int64_t)a.m * a.n;
-  splitk_sum_kernel<YDT><<<dim3((unsigned)((mn + 255) / 256)), 256, 0, s>>>(a.partial, p.splits,
-                                                                            mn, a.y);
+  kern<<<dim3((unsigned)p.grid), NW * 64, lds, s>>>(a, lv, p.phases);
   return hipGetLastError();
 }
 
@@ -1078,19 +1051,13 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
     }                                                                                         \
     return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false, false, false>(a, lv, p, s);
   switch (p.cfg) {
-    WQ_STR(22, 8, 1, 1, 1, 4)
-    WQ_STR(27, 8, 3, 1, 16, 4)
     WQ_STR(40, 8, 1, 1, 1, 2)
-    WQ_STR(41, 8, 1, 1, 1, 3)
     WQ_STR(42, 8, 1, 1, 4, 2)
     WQ_STR(43, 8, 3, 1, 16, 2)
-    WQ_STR(44, 8, 3, 1, 16, 3)
     WQ_STR(45, 8, 1, 1, 16, 2)
-    WQ_STR(46, 8, 1, 1, 16, 3)
     WQ_STR(47, 8, 1, 2, 1, 2)
     WQ_STR(50, 8, 2, 1, 16, 2)
     WQ_STR(51, 8, 4, 1, 16, 2)
-    WQ_STR(54, 8, 2, 1, 4, 2)
     WQ_STR(74, 16, 1, 1, 1, 2)
     default: return hipErrorInvalidConfiguration;
   }
@@ -1120,7 +1087,6 @@ hipError_t launch_stream_pair(const SkinnyArgs& a, const Levels& lv, const W4Pla
     WQ_PAIR(61, 8, 2, 1, 4, 2)
     WQ_PAIR(62, 8, 2, 1, 16, 2)
     WQ_PAIR(63, 8, 4, 1, 16, 2)
-    WQ_PAIR(64, 8, 6, 1, 16, 2)
     WQ_PAIR(65, 8, 8, 1, 16, 2)
     WQ_PAIR(67, 8, 6, 1, 16, 1)
     default: return hipErrorInvalidConfiguration;
@@ -1178,7 +1144,6 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
   a.sub = a.GS / a.G;
   a.zb = (a.GS + 1) / 2;
   a.y = y;
-  a.partial = static_cast<float*>(ws);
   return w->fmt == WQ_FMT_NF4 ? launch_stream<XDT, YDT, WQ_FMT_NF4>(a, lv, p, s)
                               : launch_stream<XDT, YDT, WQ_FMT_INT4_ASYM>(a, lv, p, s);
 }
@@ -1224,18 +1189,14 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   // Streaming decode configurations (NW waves, TPG row tiles, GPP groups per
   // wave and phase, MP staged activation rows, NBUF phases in flight).
   struct SCfg { int id, nw, tpg, gpp, mp, nbuf; };
-  static const SCfg scfgs[] = {
-      {22, 8, 1, 1, 1, 4},  {27, 8, 3, 1, 16, 4},  {40, 8, 1, 1, 1, 2},  {41, 8, 1, 1, 1, 3},
-      {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2},  {44, 8, 3, 1, 16, 3},  {45, 8, 1, 1, 16, 2},
-      {46, 8, 1, 1, 16, 3},  {47, 8, 1, 2, 1, 2},  {50, 8, 2, 1, 16, 2},  {51, 8, 4, 1, 16, 2},
-      {54, 8, 2, 1, 4, 2},  {74, 16, 1, 1, 1, 2}};
+  static const SCfg scfgs[] = {{40, 8, 1, 1, 1, 2},  {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2},
+                               {45, 8, 1, 1, 16, 2}, {47, 8, 1, 2, 1, 2},  {50, 8, 2, 1, 16, 2},
+                               {51, 8, 4, 1, 16, 2}, {74, 16, 1, 1, 1, 2}};
   W4Plan p;
   p.path = m > 16 ? 1 : 3;
   p.tpg = 1;
   p.gpw = 1;
   p.mp = 1;
-  p.splits = 1;
-  p.kslice = 0;
   p.cfg = 0;
   p.phases = 1;
   p.grid = 0;
@@ -1268,31 +1229,14 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
     const int64_t tpg = (ntiles + 255) / 256;
     cfg = tpg >= 4 ? 51 : tpg == 3 ? 43 : (tpg == 2 ? 50 : 45);
   }
-  int splits = 1;
-#ifdef WQ_TUNE_ENV
-  if (const char* e = getenv("WQ_DECODE")) {
-    int c = -1;
-    if (sscanf(e, "%d", &c) == 1)
-      for (const SCfg& sc : scfgs)
-        if (sc.id == c && sc.mp >= m) cfg = c;   // a schedule stages at most mp rows
-  }
-  if (const char* e = getenv("WQ_SPLIT")) {
-    int v = 0;
-    if (sscanf(e, "%d", &v) == 1 && v >= 1 && v <= 16) splits = v;
-  }
-#endif
   for (const SCfg& sc : scfgs)
     if (sc.id == cfg) {
       p.cfg = sc.id;
       p.tpg = sc.tpg;
       p.gpw = sc.gpp;
       p.mp = sc.mp;
-      p.splits = (int)std::min<int64_t>(splits, G);
-      p.kslice = (int)((G + p.splits - 1) / p.splits);
-      p.splits = (int)((G + p.kslice - 1) / p.kslice);   // no empty slice
-      p.phases = (p.kslice + sc.nw * sc.gpp - 1) / (sc.nw * sc.gpp);
+      p.phases = (int)((G + sc.nw * sc.gpp - 1) / (sc.nw * sc.gpp));
       p.grid = (int)((ntiles + sc.tpg - 1) / sc.tpg);
-      if (p.splits > 1) p.ws = (size_t)p.splits * (size_t)m * (size_t)w->n * sizeof(float);
       // staged scales must fit beside the activation ring
       if (p.szl) {
         const size_t lds = stream_lds_bytes(sc.nw, sc.tpg, sc.gpp, sc.mp, sc.nbuf, true, false,
@@ -1316,8 +1260,7 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
   // the activations are staged once for both.
   struct PCfg { int id, nw, tpg, gpp, mp, nbuf; };
   static const PCfg pcfgs[] = {{60, 8, 2, 1, 1, 2},  {61, 8, 2, 1, 4, 2}, {62, 8, 2, 1, 16, 2},
-                               {63, 8, 4, 1, 16, 2}, {64, 8, 6, 1, 16, 2},
-                               {65, 8, 8, 1, 16, 2}, {67, 8, 6, 1, 16, 1}};
+                               {63, 8, 4, 1, 16, 2}, {65, 8, 8, 1, 16, 2}, {67, 8, 6, 1, 16, 1}};
   W4Plan p = plan_w4a16(m, wg);
   p.szl = p.szl && plan_w4a16(m, wu).szl;
   if (p.path == 1) return p;
@@ -1336,22 +1279,12 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
     const int64_t th = (ntiles + 255) / 256;
     cfg = th >= 4 ? 65 : th == 3 ? 67 : (th == 2 ? 63 : 62);
   }
-#ifdef WQ_TUNE_ENV
-  if (const char* e = getenv("WQ_PAIR")) {
-    int c = -1;
-    if (sscanf(e, "%d", &c) == 1)
-      for (const PCfg& pc : pcfgs)
-        if (pc.id == c && pc.mp >= m) cfg = c;
-  }
-#endif
   for (const PCfg& pc : pcfgs)
     if (pc.id == cfg) {
       p.cfg = pc.id;
       p.tpg = pc.tpg;
       p.gpw = pc.gpp;
       p.mp = pc.mp;
-      p.splits = 1;
-      p.kslice = (int)G;
       p.phases = (int)((G + pc.nw * pc.gpp - 1) / (pc.nw * pc.gpp));
       p.grid = (int)((ntiles + pc.tpg / 2 - 1) / (pc.tpg / 2));
       p.ws = 0;

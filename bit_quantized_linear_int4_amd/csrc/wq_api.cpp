@@ -15,6 +15,9 @@ namespace {
 // elements, so every launch's grid stays within 32-bit work-item counts.
 constexpr int64_t kMaxDim = int64_t(1) << 23;
 constexpr int64_t kMaxElems = int64_t(1) << 34;
+// LLM.int8: the int32 accumulator holds 127 * 127 * k exactly for k up to
+// this bound (k multiples of 128: 133,120 at most).
+constexpr int64_t kMaxInt8K = ((int64_t(1) << 31) - 1) / (127 * 127);
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool is16(int32_t dt) { return dt == WQ_F16 || dt == WQ_BF16; }
@@ -64,7 +67,7 @@ wq_status check_weight(const wq_weight* w, bool linear_w4) {
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Workspace of wq_linear_w4a16: the schedule's partial sums, then (act-order)
+// Workspace of wq_linear_w4a16: what the schedule needs (none today), then (act-order)
 // the gathered activations.
 size_t linear_ws_bytes(size_t plan_ws, int64_t m, const wq_weight* w) {
   if (w->perm == nullptr) return plan_ws;
@@ -265,8 +268,9 @@ wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w, fl
   const wq_status st = check_weight(w, false);
   if (st != WQ_OK) return st;
   if (w->fmt != WQ_FMT_INT8_SYM_ROW) return WQ_ERR_UNSUPPORTED;
-  if (ydt != WQ_F16 && ydt != WQ_F32) return WQ_ERR_UNSUPPORTED;
-  if (!sizes_ok(m, w->k) || m > kMaxElems / w->n || w->k % 128 != 0) return WQ_ERR_SHAPE;
+  if (!is_out(ydt)) return WQ_ERR_UNSUPPORTED;
+  if (!sizes_ok(m, w->k) || m > kMaxElems / w->n || w->k % 128 != 0 || w->k > kMaxInt8K)
+    return WQ_ERR_SHAPE;
   if (!(threshold >= 0.0f)) return WQ_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;
   if (outlier_count != nullptr && !aligned(outlier_count, 4)) return WQ_ERR_ALIGN;

@@ -272,8 +272,11 @@ size_t wq_linear_int8_decomp_workspace(int64_t m, int64_t k);
  *   acc[i][j] = sum_c qx[i][c] * qw[j][c]   (exact int32)
  *   w16 = fp16(fp32(qw) * sw)               (the int8 weights dequantized;
  *                                            no fp16 copy of W is kept)
- * x: fp16 [m][k], 16-byte aligned; w: fmt INT8_SYM_ROW with k % 128 == 0;
- * y: ydt in {F16, F32}.  workspace: at least
+ * x: fp16 [m][k], 16-byte aligned; w: fmt INT8_SYM_ROW with k % 128 == 0 and
+ * k <= 133,143 (so that 127 * 127 * k, the largest possible |acc|, fits in
+ * int32; larger k returns WQ_ERR_SHAPE); y: ydt in {F16, BF16, F32}
+ * (acc * sx * sw plus the outlier sum in fp32, rounded once to ydt).
+ * workspace: at least
  * wq_linear_int8_decomp_workspace(m, k) bytes, 256-byte aligned.
  * outlier_count (device int32, nullable) receives |O|; acc_out (device int32
  * [m][n], nullable) receives acc.

@@ -243,12 +243,20 @@ def test_int8_argument_errors():
     assert call(x=None) == NULL
     assert call(ws=None) == WS
     assert call(wsb=need - 1) == WS
-    assert call(ydt=wq.BF16) == UNSUP
+    assert call(ydt=7) == UNSUP
+    assert call(ydt=wq.BF16, ws=None) == WS          # bf16 output passes the type check
     assert call(thr=-1.0) == SHAPE
     assert call(thr=float("nan")) == SHAPE
     assert call(ws=A16 + 16) == ALIGN
     w2 = _weight(fmt=wq.FMT_INT8_SYM_ROW, n=64, k=200, group=200, zeros=None)
     assert call(w=w2) == SHAPE
+    # the int32 accumulator holds 127 * 127 * k only up to k = 133,143: the
+    # largest multiple of 128 below passes the shape check, the next fails
+    big_ws = _lib().wq_linear_int8_decomp_workspace(1, 133248)
+    for k, want in ((133120, WS), (133248, SHAPE)):
+        wk = _weight(fmt=wq.FMT_INT8_SYM_ROW, n=64, k=k, group=k, zeros=None)
+        assert f(A16, 1, ctypes.byref(wk), 6.0, A16, wq.F16, None, big_ws, None, None,
+                 None) == want, k
     p = _lib().wq_int8_prepare_activations
     assert p(A16, 4, 256, 6.0, A16, A16, A16, None, A16, None) == NULL
     assert p(A16, 4, 250, 6.0, A16, A16, A16, A16, A16, None) == SHAPE

@@ -67,6 +67,7 @@ def run_decomp(x_np, w_np, thr, ydt):
 @pytest.mark.parametrize("m,n,k,n_out,thr,ydt", [
     (8, 130, 256, 3, 6.0, "f32"),
     (70, 300, 1024, 8, 6.0, "f16"),
+    (70, 300, 1024, 8, 6.0, "bf16"),
     (256, 512, 2048, 40, 6.0, "f32"),     # more than one 32-column outlier chunk
     (300, 200, 512, 5, 6.0, "f32"),       # two 256-row tiles
     (16, 256, 1024, 4, float("inf"), "f32"),

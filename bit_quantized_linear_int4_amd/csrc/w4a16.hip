@@ -170,6 +170,8 @@ __device__ __forceinline__ uint4_t unpack_biased_f16(uint32_t w) {
 
 // Decoders for one 32-bit word of 8 codes in natural order -> 8 dequantized
 // 16-bit weights, rounded once into the activation type.
+// Each pair of weights is rounded into the activation type by one
+// v_cvt_pk_{bf16,f16}_f32.
 template <int XDT>
 __device__ __forceinline__ uint4_t dequant_int4_word(uint32_t w, float z, float s) {
   uint4_t b;
@@ -177,18 +179,20 @@ __device__ __forceinline__ uint4_t dequant_int4_word(uint32_t w, float z, float 
   for (int e = 0; e < 4; ++e) {
     const float q0 = (float)((w >> (8 * e)) & 15u);
     const float q1 = (float)((w >> (8 * e + 4)) & 15u);
-    b[e] = (uint32_t)f32_to_x<XDT>((q0 - z) * s) | ((uint32_t)f32_to_x<XDT>((q1 - z) * s) << 16);
+    // (q - z) * s is exact in fp32
+    b[e] = pack2_x<XDT>((q0 - z) * s, (q1 - z) * s);
   }
   return b;
 }
+// lut2[b] = (level of code b & 15, level of code b >> 4): one 8-byte LDS
+// read per byte of codes
 template <int XDT>
-__device__ __forceinline__ uint4_t dequant_nf4_word(uint32_t w, const float* lut, float ah) {
+__device__ __forceinline__ uint4_t dequant_nf4_word(uint32_t w, const float2_t* lut2, float ah) {
   uint4_t b;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float v0 = as_f32(lut[(w >> (8 * e)) & 15u] * ah);
-    const float v1 = as_f32(lut[(w >> (8 * e + 4)) & 15u] * ah);
-    b[e] = (uint32_t)f32_to_x<XDT>(v0) | ((uint32_t)f32_to_x<XDT>(v1) << 16);
+    const float2_t l = lut2[(w >> (8 * e)) & 255u];
+    b[e] = pack2_x<XDT>(as_f32(l.x * ah), as_f32(l.y * ah));
   }
   return b;
 }
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   constexpr bool FAST = (FMT == WQ_FMT_INT4_ASYM) && (XDT == WQ_F16);
   static_assert(!SZL || FMT == WQ_FMT_INT4_ASYM, "staged scales are INT4 only");
   extern __shared__ uint4_t dsm[];
-  __shared__ float lut[16];
+  __shared__ float2_t lut2[FMT == WQ_FMT_NF4 ? 256 : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, kq = lane >> 4;
@@ -259,9 +263,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // each unit of 128, i.e. group unit * sub + lq
   const int lq = (kq * a.sub) >> 2;
   const int ntiles = (a.n + 15) / 16;
-  // every workgroup covers the whole K range: units [0, G)
-  constexpr int gbeg = 0;
-  const int gend = a.G;
+  // every workgroup covers the whole K range, units [0, G); units past G
+  // (the last phase's padding) load a clamped address and are skipped
+  auto unit = [&](int g) { return min(g, a.G - 1); };
   uint4_t* const ring = dsm + wave * NBUF * XS;
   // staged scales / zeros: per tile SCB and ZCB bytes (multiples of 1 KB)
   const int SCB = (32 * a.GS + 1023) / 1024 * 1024;
@@ -279,7 +283,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   auto second = [&](int t) { return DUAL && t >= TH; };
 
   if constexpr (FMT == WQ_FMT_NF4) {
-    if (tid < 16) lut[tid] = lv.v[tid];
+    static_assert(NW * 64 >= 256, "one thread per pair-table entry");
+    if (tid < 256) lut2[tid] = float2_t{lv.v[tid & 15], lv.v[tid >> 4]};
     __syncthreads();   // before any load is in flight: costs no wait
   }
   if constexpr (SZL) {
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     if constexpr (MP == 1) {
 #pragma unroll
       for (int gl = 0; gl < GPP; ++gl) {
-        const int g = min(gbeg + p * CG + wave * GPP + gl, a.G - 1);
+        const int g = unit(p * CG + wave * GPP + gl);
         lds_dma4(a.x + g * 128 + lane * 2, (lds_void_t*)(buf + gl * 16));
       }
       return;
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       const int m = min(sl / (16 * GPP), MP - 1);
       const int gl = (sl / 16) % GPP;
       const int c16 = (sl % 16) ^ (m & 15);
-      const int g = min(gbeg + p * CG + wave * GPP + gl, a.G - 1);
+      const int g = unit(p * CG + wave * GPP + gl);
       const int mm = min(m, a.m - 1);
       lds_dma16(a.x + (int64_t)mm * a.k + g * 128 + c16 * 8, (lds_void_t*)(buf + i * 64));
     }
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       const uint4_t* q4 = second(t) ? q4b : q4a;
 #pragma unroll
       for (int u = 0; u < GPP; ++u) {
-        const int g = min(gbeg + p * CG + wave * GPP + u, a.G - 1);
+        const int g = unit(p * CG + wave * GPP + u);
         if constexpr (CRING) {
           lds_dma16(q4 + (int64_t)row * k32 + g * 4 + kq,
                     (lds_void_t*)(wring + ((b * TPG + t) * GPP + u) * 64));
@@ -422,9 +427,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     const uint4_t* buf = ring + b * XS + mrow * (16 * GPP);
 #pragma unroll
     for (int u = 0; u < GPP; ++u) {
-      const int g = gbeg + p * CG + wave * GPP + u;
-      const int gq = g * a.sub + lq;            // this lane's INT4 group
-      if (g < gend) {
+      const int gl = p * CG + wave * GPP + u;   // logical unit
+      const int gq = unit(gl) * a.sub + lq;     // this lane's INT4 group
+      if (gl < a.G) {
         if constexpr (SZL) {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
                 const float z = (float)((gq & 1) ? (zv[b][t][u] >> 4) : (zv[b][t][u] & 15u));
                 bw = dequant_int4_word<XDT>(wv[b][t][u][j], z, sv[b][t][u]);
               } else {
-                bw = dequant_nf4_word<XDT>(wv[b][t][u][j], lut, sv[b][t][u]);
+                bw = dequant_nf4_word<XDT>(wv[b][t][u][j], lut2, sv[b][t][u]);
               }
               acc[t] = mfma16<XDT>(A[j], bw, acc[t]);
             }

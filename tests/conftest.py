@@ -28,3 +28,23 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+# Max-relative errors of the full-size workload parity cases, printed at the
+# end of the run (so they show in `pytest -q` output as well).
+_MARGINS = {}
+
+
+@pytest.fixture
+def record_margin():
+    def rec(name, rel, tol=2e-3):
+        _MARGINS[name] = (rel, tol)
+    return rec
+
+
+def pytest_terminal_summary(terminalreporter):
+    if not _MARGINS:
+        return
+    terminalreporter.write_sep("-", "max|y - y_ref| / max|y_ref| at the workload shapes")
+    for name, (rel, tol) in sorted(_MARGINS.items()):
+        terminalreporter.write_line(f"{name:48s} {rel:.3e}  ({rel / tol:.0%} of {tol:.0e})")

@@ -349,3 +349,44 @@ def test_deterministic_repeats():
     y1, qw = run_linear(x, w, "f16", "f32")
     y2, _ = run_linear(x, w, "f16", "f32", qw=qw)
     assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("case", ["decode_m1", "mlp_gate_up_pair", "mlp_down", "prefill_q",
+                                  "prefill_up"])
+def test_workload_full_shape_margins(case, record_margin):
+    """The benchmarked layers at full size and with the benchmark's own
+    seeded inputs (fp32 outputs): single-layer decode at M = 1, the MLP
+    decode step at M = 16 (gate + up as one pair call, down at K = 11008,
+    both with the fixed outlier channels), and the prefill q and up layers at
+    M = 2048 (64 sampled token rows, every output column).  The max-relative
+    error of each is recorded and printed at the end of the run."""
+    say(f"workload_margin {case}")
+    if case == "decode_m1":
+        d = workloads.decode_m1()
+        y, _ = run_linear(d["x"], d["w"], "f16", "f32")
+        rel = check_close(y, oracle_linear(d["x"], d["w"], "f16"), "f32")
+        record_margin("decode M=1 4096x4096 (fp16 fast path)", rel)
+    elif case == "mlp_gate_up_pair":
+        (_, x_np, wg_np), (_, _, wu_np) = workloads.mlp_decode(layers=("gate", "up"))
+        qg, qu = gpu_quantize_int4(dev_f16(wg_np)), gpu_quantize_int4(dev_f16(wu_np))
+        yg = torch.empty((16, 11008), dtype=torch.float32, device="cuda")
+        yu = torch.empty_like(yg)
+        wq.wq_linear_w4a16_gate_up(dev_f16(x_np), qg, qu, yg, yu, act=0)
+        torch.cuda.synchronize()
+        rg = check_close(to_np(yg), oracle_linear(x_np, wg_np, "f16"), "f32")
+        ru = check_close(to_np(yu), oracle_linear(x_np, wu_np, "f16"), "f32")
+        record_margin("MLP gate (pair) M=16 11008x4096, outliers", rg)
+        record_margin("MLP up (pair) M=16 11008x4096, outliers", ru)
+        rel = max(rg, ru)
+    elif case == "mlp_down":
+        _, x_np, w_np = workloads.mlp_decode()[2]
+        y, _ = run_linear(x_np, w_np, "f16", "f32")
+        rel = check_close(y, oracle_linear(x_np, w_np, "f16"), "f32")
+        record_margin("MLP down M=16 4096x11008, outliers", rel)
+    else:
+        (_, x_np, w_np), = workloads.prefill(layers=(case.split("_")[1],))
+        y, _ = run_linear(x_np, w_np, "f16", "f32")
+        rows = np.random.default_rng(1).choice(2048, size=64, replace=False)
+        rel = check_close(y[rows], oracle_linear(x_np, w_np, "f16", rows=rows), "f32")
+        record_margin(f"prefill {case.split('_')[1]} M=2048 (64 rows sampled)", rel)
+    say(f"  max-rel {rel:.2e}")

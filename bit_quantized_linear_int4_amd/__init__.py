@@ -21,7 +21,8 @@ __all__ = [
     "wq_linear_w4a16_workspace", "wq_linear_w4a16", "wq_linear_w4a16_gate_up",
     "wq_permute_columns", "wq_scale_columns",
     "wq_int8_prepare_activations", "wq_linear_int8_decomp_workspace",
-    "wq_linear_int8_decomp", "wq_dequantize", "wq_status_string",
+    "wq_linear_int8_decomp", "wq_linear_int8_decomp_noalloc", "wq_dequantize",
+    "wq_status_string",
     "alloc_int4", "alloc_nf4", "alloc_fp4", "alloc_int8", "library_path", "FMT_FP4",
 ]
 
@@ -85,6 +86,8 @@ def _load():
         "wq_linear_int8_decomp_workspace": (ctypes.c_size_t, [c_i64, c_i64]),
         "wq_linear_int8_decomp": (c_i32, [c_vp, c_i64, wp, c_f, c_vp, c_i32, c_vp,
                                           ctypes.c_size_t, c_vp, c_vp, c_vp]),
+        "wq_linear_int8_decomp_noalloc": (c_i32, [c_vp, c_i64, wp, c_f, c_vp, c_i32, c_vp, c_vp,
+                                                  c_vp]),
         "wq_dequantize": (c_i32, [wp, c_vp, c_i32, c_vp]),
         "wq_permute_columns": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_vp, c_vp]),
         "wq_scale_columns": (c_i32, [c_vp, c_i32, c_i64, c_i64, c_vp, c_vp, c_vp]),
@@ -426,6 +429,22 @@ def wq_linear_int8_decomp(x, weight, threshold, y, workspace, outlier_count=None
                                        _ptr(y), _dt(y), _ptr(workspace), ws_bytes,
                                        _ptr(outlier_count), _ptr(acc_out), _stream(stream, x))
     _check(st, "wq_linear_int8_decomp")
+
+
+def wq_linear_int8_decomp_noalloc(x, weight, threshold, y, outlier_count=None, acc_out=None,
+                                  stream=None):
+    what = "wq_linear_int8_decomp_noalloc"
+    m, ts = _check_linear(what, x, weight, [("y", y)])
+    if outlier_count is not None:
+        _dense(what, "outlier_count", outlier_count, 4)
+    if acc_out is not None:
+        _dense(what, "acc_out", acc_out, 4 * m * weight.n)
+    _on_gpu(what, outlier_count, acc_out, *ts)
+    d = weight.descriptor()
+    st = _load().wq_linear_int8_decomp_noalloc(_ptr(x), m, ctypes.byref(d), float(threshold),
+                                               _ptr(y), _dt(y), _ptr(outlier_count),
+                                               _ptr(acc_out), _stream(stream, x))
+    _check(st, what)
 
 
 def wq_permute_columns(src, perm, dst, stream=None):

@@ -2,8 +2,10 @@
 //
 // Every check runs before the first HIP call, so an error other than
 // WQ_ERR_HIP means nothing was enqueued.  No C++ exception crosses the ABI.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.h"
 
@@ -261,9 +263,15 @@ wq_status wq_int8_prepare_activations(const void* x, int64_t m, int64_t k, float
                                         idx, count, qx, sx, static_cast<hipStream_t>(stream)));
 }
 
-wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w, float threshold,
-                                void* y, int32_t ydt, void* workspace, size_t ws_bytes,
-                                int32_t* outlier_count, int32_t* acc_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the two LLM.int8 entry points (everything but
+// the workspace).
+wq_status check_int8_decomp(const void* x, int64_t m, const wq_weight* w, float threshold,
+                            const void* y, int32_t ydt, const int32_t* outlier_count,
+                            const int32_t* acc_out) {
   if (x == nullptr || y == nullptr) return WQ_ERR_NULL;
   const wq_status st = check_weight(w, false);
   if (st != WQ_OK) return st;
@@ -275,18 +283,23 @@ wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w, fl
   if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;
   if (outlier_count != nullptr && !aligned(outlier_count, 4)) return WQ_ERR_ALIGN;
   if (acc_out != nullptr && !aligned(acc_out, 4)) return WQ_ERR_ALIGN;
-  const size_t need = wq_linear_int8_decomp_workspace(m, w->k);
-  if (workspace == nullptr || ws_bytes < need) return WQ_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
+  return WQ_OK;
+}
+
+// The two launches of the decomposition with the scratch at `base`
+// (256-byte aligned, at least wq_linear_int8_decomp_workspace(m, k) bytes).
+// Every scratch byte a kernel reads was written earlier in the same call, so
+// the scratch needs no clearing.
+wq_status run_int8_decomp(const void* x, int64_t m, const wq_weight* w, float threshold, void* y,
+                          int32_t ydt, char* base, int32_t* outlier_count, int32_t* acc_out,
+                          hipStream_t s) {
   auto up = [](size_t v) { return (v + 255) & ~size_t(255); };
   const size_t k = (size_t)w->k;
-  char* base = static_cast<char*>(workspace);
   uint8_t* mask = reinterpret_cast<uint8_t*>(base);
   int32_t* idx = reinterpret_cast<int32_t*>(base + up(k));
   int32_t* count = reinterpret_cast<int32_t*>(base + up(k) + up(4 * k));
   int8_t* qx = reinterpret_cast<int8_t*>(base + up(k) + up(4 * k) + up(4));
   float* sx = reinterpret_cast<float*>(base + up(k) + up(4 * k) + up(4) + up((size_t)m * k));
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   hipError_t e = launch_int8_prepare(xp, m, w->k, threshold, mask, idx, count, qx, sx, s);
   if (e != hipSuccess) return WQ_ERR_HIP;
@@ -297,6 +310,62 @@ wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w, fl
     if (e != hipSuccess) return WQ_ERR_HIP;
   }
   return WQ_OK;
+}
+
+// Scratch of wq_linear_int8_decomp_noalloc: a device array of fixed size,
+// one copy per GPU, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: kernels get the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in `g_scratch`.
+constexpr size_t kNoAllocScratchBytes = WQ_INT8_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address, or nullptr if it cannot be had.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w, float threshold,
+                                void* y, int32_t ydt, void* workspace, size_t ws_bytes,
+                                int32_t* outlier_count, int32_t* acc_out, void* stream) {
+  const wq_status st = check_int8_decomp(x, m, w, threshold, y, ydt, outlier_count, acc_out);
+  if (st != WQ_OK) return st;
+  const size_t need = wq_linear_int8_decomp_workspace(m, w->k);
+  if (workspace == nullptr || ws_bytes < need) return WQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
+  return run_int8_decomp(x, m, w, threshold, y, ydt, static_cast<char*>(workspace),
+                         outlier_count, acc_out, static_cast<hipStream_t>(stream));
+}
+
+wq_status wq_linear_int8_decomp_noalloc(const void* x, int64_t m, const wq_weight* w,
+                                        float threshold, void* y, int32_t ydt,
+                                        int32_t* outlier_count, int32_t* acc_out,
+                                        void* stream) {
+  const wq_status st = check_int8_decomp(x, m, w, threshold, y, ydt, outlier_count, acc_out);
+  if (st != WQ_OK) return st;
+  if (wq_linear_int8_decomp_workspace(m, w->k) > kNoAllocScratchBytes) return WQ_ERR_WORKSPACE;
+  void* base = device_scratch();
+  if (base == nullptr) return WQ_ERR_HIP;
+  return run_int8_decomp(x, m, w, threshold, y, ydt, static_cast<char*>(base), outlier_count,
+                         acc_out, static_cast<hipStream_t>(stream));
 }
 
 wq_status wq_permute_columns(const void* src, int32_t dt, int64_t rows, int64_t k,

@@ -36,7 +36,10 @@
  *  - Rounding: every "round" is round-half-to-even; every division is an
  *    IEEE fp32 division; 16-bit conversions round to nearest even.
  *  - The library's only mutable global state is the per-kernel LDS limit it
- *    raises once (atomically) on first use; calls are thread-safe.
+ *    raises once (atomically) on first use and, per GPU, the address of the
+ *    no-allocation scratch array (looked up once, under a lock); calls are
+ *    thread-safe, except that wq_linear_int8_decomp_noalloc calls sharing a
+ *    GPU's scratch must not overlap.
  */
 #ifndef WQ_H
 #define WQ_H
@@ -286,6 +289,27 @@ wq_status wq_linear_int8_decomp(const void* x, int64_t m, const wq_weight* w,
                                 void* workspace, size_t ws_bytes,
                                 int32_t* outlier_count, int32_t* acc_out,
                                 void* stream);
+
+/*
+ * wq_linear_int8_decomp for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops and harnesses that forbid
+ * allocation): the same computation and kernels, with no workspace
+ * argument.  The scratch (outlier mask and list, count, int8 activations,
+ * row scales) is a device array of WQ_INT8_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; the call allocates and
+ * frees nothing.  Arguments, results and errors as wq_linear_int8_decomp;
+ * calls whose wq_linear_int8_decomp_workspace(m, k) exceeds the array return
+ * WQ_ERR_WORKSPACE, and WQ_ERR_HIP also reports a failure to find the
+ * array on the current device.  Every call on one GPU uses that GPU's
+ * array and leaves its contents behind (no byte of it needs to start at
+ * zero): calls that overlap on one GPU -- on different streams or from
+ * different host threads -- race, and the caller must order them.
+ */
+#define WQ_INT8_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+wq_status wq_linear_int8_decomp_noalloc(const void* x, int64_t m, const wq_weight* w,
+                                        float threshold, void* y, int32_t ydt,
+                                        int32_t* outlier_count, int32_t* acc_out,
+                                        void* stream);
 
 /*
  * Column gather (act-order reordering, [P1] 3.2, [P4] 3.2):

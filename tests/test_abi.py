@@ -263,6 +263,27 @@ def test_int8_argument_errors():
     assert p(A16, 4, 256, 6.0, A16 + 4, A16, A16, A16, A16, None) == ALIGN
 
 
+def test_int8_noalloc_argument_errors():
+    """The no-allocation entry point checks its arguments like the workspace
+    one, and rejects sizes whose scratch exceeds the library's fixed array
+    (before any HIP call)."""
+    f = _lib().wq_linear_int8_decomp_noalloc
+    w = _weight(fmt=wq.FMT_INT8_SYM_ROW, n=64, k=8192, group=8192, zeros=None)
+    limit = 8 << 20
+
+    def call(x=A16, m=4, thr=6.0, y=A16, ydt=wq.F16):
+        return f(x, m, ctypes.byref(w), thr, y, ydt, None, None, None)
+
+    assert call(x=None) == NULL
+    assert call(ydt=7) == UNSUP
+    assert call(thr=-1.0) == SHAPE
+    assert call(y=ODD) == ALIGN
+    # the 70B layer's 256 tokens fit; 1024 tokens of k = 8192 do not
+    assert _lib().wq_linear_int8_decomp_workspace(256, 8192) <= limit
+    assert _lib().wq_linear_int8_decomp_workspace(1024, 8192) > limit
+    assert call(m=1024) == WS
+
+
 def test_dequantize_argument_errors():
     f = _lib().wq_dequantize
     assert f(ctypes.byref(_weight()), None, wq.F16, None) == NULL

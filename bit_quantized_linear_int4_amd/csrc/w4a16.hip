@@ -140,6 +140,20 @@ struct Levels {
   float v[16];
 };
 
+// Per-tile metadata staged in LDS by the decode kernel (SZL), in bytes.
+// INT4: the 16 rows' fp16 scales (a) and zero-point bytes (b), each rounded
+// up to the 1 KB direct loads that bring them in.  NF4 with double-quantized
+// absmax: the int8 absmax codes of the 16 rows' blocks (a: 16 * k/64
+// contiguous bytes, 1 KB loads) and the fp32 second-level scales that cover
+// them (b: at most 16 * k/64 / 256 + 2 values, plain loads).
+__host__ __device__ inline int staged_a_bytes(int fmt, int GS, int k) {
+  return fmt == WQ_FMT_NF4 ? (16 * (k / 64) + 1023) / 1024 * 1024 : (32 * GS + 1023) / 1024 * 1024;
+}
+__host__ __device__ inline int staged_c2_count(int k) { return 16 * (k / 64) / 256 + 2; }
+__host__ __device__ inline int staged_b_bytes(int fmt, int zb, int k) {
+  return fmt == WQ_FMT_NF4 ? (staged_c2_count(k) * 4 + 15) / 16 * 16 : (16 * zb + 1023) / 1024 * 1024;
+}
+
 // c in a VGPR, opaque to the optimizer (the empty asm emits nothing).
 __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
   asm("" : "+v"(c));
@@ -253,7 +267,6 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   constexpr int LPU = SZL ? 1 : 3;                         // loads per code unit
   constexpr int WU = TPG * GPP * LPU;                      // code-side loads per phase
   constexpr bool FAST = (FMT == WQ_FMT_INT4_ASYM) && (XDT == WQ_F16);
-  static_assert(!SZL || FMT == WQ_FMT_INT4_ASYM, "staged scales are INT4 only");
   extern __shared__ uint4_t dsm[];
   __shared__ float2_t lut2[FMT == WQ_FMT_NF4 ? 256 : 1];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -265,11 +278,15 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   const int ntiles = (a.n + 15) / 16;
   // every workgroup covers the whole K range, units [0, G); units past G
   // (the last phase's padding) load a clamped address and are skipped
-  auto unit = [&](int g) { return min(g, a.G - 1); };
+  const int nun = a.G;
+  auto unit = [&](int g) { return min(g, nun - 1); };
   uint4_t* const ring = dsm + wave * NBUF * XS;
-  // staged scales / zeros: per tile SCB and ZCB bytes (multiples of 1 KB)
-  const int SCB = (32 * a.GS + 1023) / 1024 * 1024;
-  const int ZCB = (16 * a.zb + 1023) / 1024 * 1024;
+  // staged metadata per tile: SCB and ZCB bytes (INT4 scales and zero
+  // points; NF4 absmax codes and second-level scales)
+  const int SCB = staged_a_bytes(FMT, a.GS, a.k);
+  const int ZCB = staged_b_bytes(FMT, a.zb, a.k);
+  const int bpr = a.k / 64;                  // NF4 blocks per row
+  const int NC2 = staged_c2_count(a.k);      // NF4 second-level scales per tile
   uint8_t* const scl = reinterpret_cast<uint8_t*>(dsm + NW * NBUF * XS);
   uint8_t* const zcl = scl + TPG * SCB;
   // CRING: the codes also arrive through LDS (per-wave ring, 1 KB per unit:
@@ -285,19 +302,33 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   if constexpr (FMT == WQ_FMT_NF4) {
     static_assert(NW * 64 >= 256, "one thread per pair-table entry");
     if (tid < 256) lut2[tid] = float2_t{lv.v[tid & 15], lv.v[tid >> 4]};
-    __syncthreads();   // before any load is in flight: costs no wait
+    if constexpr (SZL) {
+      // the second-level scales of each tile's blocks (indices clamped to
+      // the last one), with plain loads before any direct load is issued
+      const int64_t n2 = ((int64_t)a.n * bpr + 255) >> 8;
+      float* c2l = reinterpret_cast<float*>(zcl);
+      for (int i = tid; i < TPG * NC2; i += NW * 64) {
+        const int t = i / NC2, j = i % NC2;
+        const int64_t c0 = ((int64_t)tile_of(t) * 16 * bpr) >> 8;
+        c2l[t * (ZCB / 4) + j] = a.scales2[min(c0 + j, n2 - 1)];
+      }
+    }
+    __syncthreads();   // before any direct load is in flight: costs no wait
   }
   if constexpr (SZL) {
-    // 1 KB direct loads of the tiles' scale and zero rows, spread over the
-    // waves; chunks past the end of a buffer reload its last 16 bytes
-    const int nsc = SCB / 1024, nzc = ZCB / 1024, per = nsc + nzc;
-    const int64_t sbytes = (int64_t)a.n * a.GS * 2, zbytes = (int64_t)a.n * a.zb;
+    // 1 KB direct loads of the tiles' scale and zero rows (NF4: absmax
+    // codes), spread over the waves; chunks past the end of a buffer reload
+    // its last 16 bytes
+    constexpr bool NF = FMT == WQ_FMT_NF4;
+    const int nsc = SCB / 1024, nzc = NF ? 0 : ZCB / 1024, per = nsc + nzc;
+    const int64_t sbytes = NF ? (int64_t)a.n * bpr : (int64_t)a.n * a.GS * 2;
+    const int64_t zbytes = (int64_t)a.n * a.zb;
     for (int i = wave; i < TPG * per; i += NW) {
       const int t = i / per, j = i % per;
       const int tile = tile_of(t);
       const bool isz = j >= nsc;
       const int jj = isz ? j - nsc : j;
-      const int64_t off = (int64_t)tile * 16 * (isz ? a.zb : 2 * a.GS) + jj * 1024 + lane * 16;
+      const int64_t off = (int64_t)tile * 16 * (isz ? a.zb : (NF ? bpr : 2 * a.GS)) + jj * 1024 + lane * 16;
       const int64_t lim = (isz ? zbytes : sbytes) - 16;
       const uint8_t* zsrc = second(t) ? a.zeros_b : a.zeros;
       const uint8_t* ssrc = static_cast<const uint8_t*>(second(t) ? a.scales_b : a.scales);
@@ -429,14 +460,23 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     for (int u = 0; u < GPP; ++u) {
       const int gl = p * CG + wave * GPP + u;   // logical unit
       const int gq = unit(gl) * a.sub + lq;     // this lane's INT4 group
-      if (gl < a.G) {
+      if (gl < nun) {
         if constexpr (SZL) {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
             if constexpr (CRING) wv[b][t][u] = wring[((b * TPG + t) * GPP + u) * 64 + lane];
-            const uint16_t sc = *reinterpret_cast<const uint16_t*>(scl + t * SCB + (nl * a.GS + gq) * 2);
-            sv[b][t][u] = f16_bits_to_f32(sc);
-            zv[b][t][u] = zcl[t * ZCB + nl * a.zb + (gq >> 1)];
+            if constexpr (FMT == WQ_FMT_NF4) {
+              // absmax of this lane's block, fp32(q8) * c2 as the double
+              // quantization defines it
+              const int rb = nl * bpr + 2 * unit(gl) + (kq >> 1);   // block within the tile
+              const int64_t tb = (int64_t)tile_of(t) * 16 * bpr;
+              const float c2 = reinterpret_cast<const float*>(zcl + t * ZCB)[((tb + rb) >> 8) - (tb >> 8)];
+              sv[b][t][u] = (float)reinterpret_cast<const int8_t*>(scl + t * SCB)[rb] * c2;
+            } else {
+              const uint16_t sc = *reinterpret_cast<const uint16_t*>(scl + t * SCB + (nl * a.GS + gq) * 2);
+              sv[b][t][u] = f16_bits_to_f32(sc);
+              zv[b][t][u] = zcl[t * ZCB + nl * a.zb + (gq >> 1)];
+            }
           }
         }
         uint4_t A[4];
@@ -534,19 +574,22 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   __syncthreads();
   constexpr int NV = TPG * 4 * kWave;
   constexpr int NH = TH * 4 * kWave;                 // the second matrix's sums start here
+  // the sum of entry i of the NV results over the waves, in a fixed order
+  auto total = [&](int i) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[i + w * NV];
+    return v;
+  };
   for (int i = tid; i < NH; i += NW * 64) {
     const int te = i / kWave, l = i % kWave, t = te / 4, e = te % 4;
     const int mm = (l >> 4) * 4 + e;
     const int tile = (int)blockIdx.x + t * (int)gridDim.x;
     const int nn = tile * 16 + (l & 15);
     if (mm < a.m && tile < ntiles && nn < a.n) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[i + w * NV];
+      const float v = total(i);
       if constexpr (DUAL) {
-        float v2 = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) v2 += red[i + NH + w * NV];
+        const float v2 = total(i + NH);
         const int64_t o = (int64_t)mm * a.n + nn;
         if (a.act) {
           store_y<YDT>(a.y, o, v / (1.0f + expf(-v)) * v2);   // silu(gate) * up
@@ -563,11 +606,11 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
 
 // Dynamic LDS bytes of one stream_kernel workgroup.
 inline size_t stream_lds_bytes(int nw, int tpg, int gpp, int mp, int nbuf, bool szl, bool dual,
-                               int G, int zb) {
+                               int fmt, int GS, int zb, int k) {
   const size_t xs = (size_t)((mp * gpp * 16 + 63) / 64 * 64) * 16;
   size_t b = (size_t)nw * nbuf * xs;
   if (szl)
-    b += (size_t)tpg * ((32 * G + 1023) / 1024 * 1024 + (16 * zb + 1023) / 1024 * 1024) +
+    b += (size_t)tpg * (staged_a_bytes(fmt, GS, k) + staged_b_bytes(fmt, zb, k)) +
          (dual ? 0 : (size_t)nw * nbuf * tpg * gpp * 1024);
   const size_t red = (size_t)nw * tpg * 4 * 64 * 4;
   return b > red ? b : red;
@@ -1018,7 +1061,7 @@ template <int XDT, int YDT, int FMT, int NW, int TPG, int GPP, int MP, int NBUF,
           bool DUAL, bool SG>
 hipError_t launch_stream_t(const SkinnyArgs& a, const Levels& lv, const W4Plan& p, hipStream_t s) {
   auto kern = stream_kernel<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, SZL, DUAL, SG>;
-  const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, DUAL, a.GS, a.zb);
+  const size_t lds = stream_lds_bytes(NW, TPG, GPP, MP, NBUF, SZL, DUAL, FMT, a.GS, a.zb, a.k);
   if (a.m > MP) return hipErrorInvalidValue;   // rows past MP are never staged
   if (lds > 160 * 1024 - 256) return hipErrorInvalidConfiguration;
   // raise the dynamic LDS limit of this instantiation when a launch needs
@@ -1050,10 +1093,10 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
               a, lv, p, s);                                                                   \
         }                                                                                     \
       }                                                                                       \
-      if (p.szl)                                                                              \
-        return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, true, false, false>(     \
-            a, lv, p, s);                                                                     \
     }                                                                                         \
+    if (p.szl)                                                                                \
+      return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, true, false, false>(      \
+          a, lv, p, s);                                                                       \
     return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false, false, false>(a, lv, p, s);
   switch (p.cfg) {
     WQ_STR(40, 8, 1, 1, 1, 2)
@@ -1135,7 +1178,7 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
       gemm_kernel<WQ_FMT_INT4_ASYM, XDT, YDT><<<grid, 256, 0, s>>>(a, lv);
     return hipGetLastError();
   }
-  SkinnyArgs a;
+  SkinnyArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.codes = static_cast<const uint32_t*>(w->codes);
   a.scales = w->scales;
@@ -1211,6 +1254,11 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
           ((uintptr_t)w->zeros % 16) == 0 && (w->n * GS * 2) % 16 == 0 &&
           (w->n * ((GS + 1) / 2)) % 16 == 0;
   if (p.path == 1) return p;
+  // NF4/FP4 decode: the int8 absmax codes of a tile's blocks staged by 1 KB
+  // direct loads (16-byte aligned buffer, a multiple of 16 bytes long)
+  if (w->fmt == WQ_FMT_NF4)
+    p.szl = w->scales2 != nullptr && ((uintptr_t)w->scales % 16) == 0 &&
+            (w->n * (w->k / 64)) % 16 == 0;
   const int64_t G = w->k / 128;
   const int64_t ntiles = (w->n + 15) / 16;
   // measured on MI355X (graph-replayed calls of the 7B/8B decode shapes);
@@ -1245,7 +1293,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
       // staged scales must fit beside the activation ring
       if (p.szl) {
         const size_t lds = stream_lds_bytes(sc.nw, sc.tpg, sc.gpp, sc.mp, sc.nbuf, true, false,
-                                            (int)GS, (int)((GS + 1) / 2));
+                                            w->fmt, (int)GS, (int)((GS + 1) / 2), (int)w->k);
         if (lds > 160 * 1024 - 256) p.szl = false;
       }
     }
@@ -1294,8 +1342,9 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
       p.grid = (int)((ntiles + pc.tpg / 2 - 1) / (pc.tpg / 2));
       p.ws = 0;
       const int64_t GSp = int4_groups(wg);
-      if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true, (int)GSp,
-                                    (int)((GSp + 1) / 2)) > 160 * 1024 - 256)
+      if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true,
+                                    WQ_FMT_INT4_ASYM, (int)GSp, (int)((GSp + 1) / 2),
+                                    (int)wg->k) > 160 * 1024 - 256)
         p.szl = false;
     }
   return p;

@@ -78,6 +78,13 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, lds_void_t* lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(l) : "memory");
 }
 
+// The same with the non-temporal cache policy: for streamed data that no
+// other load of the kernel reads again (the decode kernels' codes at M = 1).
+__device__ __forceinline__ void lds_dma16_nt(const void* gaddr, lds_void_t* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gaddr), "{m0}"(l) : "memory");
+}
+
 // The 4-byte form (global_load_lds_dword): lane l's 4 bytes land at
 // lds + 4*l, 256 bytes per wave.
 __device__ __forceinline__ void lds_dma4(const void* gaddr, lds_void_t* lds) {

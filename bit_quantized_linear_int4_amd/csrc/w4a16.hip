@@ -255,9 +255,11 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // of the first (gate) matrix, tile TH + t the same rows of the second (up)
   constexpr int TH = DUAL ? TPG / 2 : TPG;                 // row tiles per workgroup
   static_assert(!DUAL || (TPG % 2 == 0 && FMT == WQ_FMT_INT4_ASYM), "pairs are INT4");
-  // codes through a per-wave LDS ring (staged scales, one matrix); else in
-  // registers
-  constexpr bool CRING = SZL && !DUAL;
+  // codes through a per-wave LDS ring (with staged scales), else in
+  // registers; pairs with 16 staged rows keep them in registers (15.2
+  // against 15.8 us through LDS for the 11008-row pair at M = 16, while at
+  // M = 1 the ring is faster, 13.1 against 14.1 us; A/B in one run)
+  constexpr bool CRING = SZL && (!DUAL || MP == 1);
   constexpr int CG = NW * GPP;                             // groups per phase
   constexpr int XS = (MP * GPP * 16 + 63) / 64 * 64;       // slots per wave buffer
   // direct activation loads per phase: 1 KB each, or with one staged row
@@ -385,8 +387,13 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       for (int u = 0; u < GPP; ++u) {
         const int g = unit(p * CG + wave * GPP + u);
         if constexpr (CRING) {
-          lds_dma16(q4 + (int64_t)row * k32 + g * 4 + kq,
-                    (lds_void_t*)(wring + ((b * TPG + t) * GPP + u) * 64));
+          // one staged activation row (M = 1): the non-temporal policy for
+          // the codes (1.5-2.5% faster on the M = 1 layers, A/B in one run;
+          // with 16 rows, where the activations are re-read from L2 far
+          // more, 4% slower)
+          const uint4_t* src = q4 + (int64_t)row * k32 + g * 4 + kq;
+          lds_void_t* dst = (lds_void_t*)(wring + ((b * TPG + t) * GPP + u) * 64);
+          if constexpr (MP == 1) lds_dma16_nt(src, dst); else lds_dma16(src, dst);
         } else {
           wv[b][t][u] = q4[(int64_t)row * k32 + g * 4 + kq];
         }
@@ -564,16 +571,23 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   }
   vm_wait<0>();   // clamped loads of unused prologue phases
 
-  // fixed-order sum of the NW waves' partial results
+  // fixed-order sum of the NW waves' partial results.  Lane l holds rows
+  // (l >> 4) * 4 + e of its 16 x 16 tile; with MP staged rows only the
+  // entries of rows below MP can be stored (MP <= 4: lanes 0-15 and e < MP),
+  // so only those go through LDS and get summed.
+  constexpr int EV = MP < 4 ? MP : 4;                // entries e that can be stored
+  constexpr int LV = MP <= 4 ? 16 : kWave;           // lanes that can
   __syncthreads();
   float* red = reinterpret_cast<float*>(dsm);
+  if (LV == kWave || lane < LV) {
 #pragma unroll
-  for (int t = 0; t < TPG; ++t)
+    for (int t = 0; t < TPG; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[((wave * TPG + t) * 4 + e) * kWave + lane] = acc[t][e];
+      for (int e = 0; e < EV; ++e) red[((wave * TPG + t) * EV + e) * LV + lane] = acc[t][e];
+  }
   __syncthreads();
-  constexpr int NV = TPG * 4 * kWave;
-  constexpr int NH = TH * 4 * kWave;                 // the second matrix's sums start here
+  constexpr int NV = TPG * EV * LV;
+  constexpr int NH = TH * EV * LV;                   // the second matrix's sums start here
   // the sum of entry i of the NV results over the waves, in a fixed order
   auto total = [&](int i) {
     float v = 0.f;
@@ -582,7 +596,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
     return v;
   };
   for (int i = tid; i < NH; i += NW * 64) {
-    const int te = i / kWave, l = i % kWave, t = te / 4, e = te % 4;
+    const int te = i / LV, l = i % LV, t = te / EV, e = te % EV;
     const int mm = (l >> 4) * 4 + e;
     const int tile = (int)blockIdx.x + t * (int)gridDim.x;
     const int nn = tile * 16 + (l & 15);
@@ -611,8 +625,8 @@ inline size_t stream_lds_bytes(int nw, int tpg, int gpp, int mp, int nbuf, bool 
   size_t b = (size_t)nw * nbuf * xs;
   if (szl)
     b += (size_t)tpg * (staged_a_bytes(fmt, GS, k) + staged_b_bytes(fmt, zb, k)) +
-         (dual ? 0 : (size_t)nw * nbuf * tpg * gpp * 1024);
-  const size_t red = (size_t)nw * tpg * 4 * 64 * 4;
+         (dual && mp > 1 ? 0 : (size_t)nw * nbuf * tpg * gpp * 1024);
+  const size_t red = (size_t)nw * tpg * 4 * 64 * 4;   // an upper bound of the sums' LDS
   return b > red ? b : red;
 }
 
@@ -808,6 +822,7 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv
   static_assert(FMT == WQ_FMT_INT4_ASYM || SUB == 1, "NF4 blocks: one unit of 128 = two blocks");
   constexpr int NW = NWG, BM = 128, BN = 256;
   constexpr int NF = BN / 16 / NW;               // 16-row code tiles per wave (n)
+  constexpr int MI = BM / 16;                    // 16-row activation tiles per wave (m): all
   constexpr int XBUF = BM * 16;                  // 16-byte chunks per activation buffer
   constexpr int WBUF = BN * 4;                   // 16-byte chunks per code buffer
   constexpr int XI = XBUF / 64 / NW;             // activation loads per wave and group
@@ -916,9 +931,9 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv
     for (int t = 0; t < WI; ++t) lds_dma16(base + woff[t], (lds_void_t*)(buf + (t * NW + wave) * 64));
   };
 
-  float4_t acc[8][NF];
+  float4_t acc[MI][NF];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NF; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -966,11 +981,25 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv
         zf[j] = 0.0f;
       }
     }
+    // activation fragments of chunk s; with the INT4 fp16 decoder those of
+    // chunk s + 1 are read while chunk s multiplies (66.98 against 68.75 us
+    // on 2048 x 4096 x 4096; the NF4 decoder, whose table reads share the
+    // LDS, measured 3.6% slower with it), A/B in one run
+    constexpr int AB = FAST ? 2 : 1;
+    uint4_t AA[AB][MI];
+    auto read_a = [&](uint4_t (&dst)[MI], int s) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) dst[i] = xcur[(i * 16 + nl) * 16 + ((kq * 4 + s) ^ nl)];
+    };
+    if constexpr (AB == 2) read_a(AA[0], 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4_t A[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) A[i] = xcur[(i * 16 + nl) * 16 + ((kq * 4 + s) ^ nl)];
+      if constexpr (AB == 2) {
+        if (s + 1 < 4) read_a(AA[(s + 1) & 1], s + 1);
+      } else {
+        read_a(AA[0], s);
+      }
+      const uint4_t(&A)[MI] = AA[AB == 2 ? (s & 1) : 0];
 #pragma unroll
       for (int j = 0; j < NF; ++j) {
         const uint32_t w = wv[j][s];
@@ -1004,14 +1033,14 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv
           }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i][j] = mfma16<XDT>(A[i], B, acc[i][j]);
+        for (int i = 0; i < MI; ++i) acc[i][j] = mfma16<XDT>(A[i], B, acc[i][j]);
       }
     }
   }
   vm_wait<0>();   // the clamped loads past the last group
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NF; ++j)
 #pragma unroll

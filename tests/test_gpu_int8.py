@@ -74,6 +74,8 @@ def run_decomp(x_np, w_np, thr, ydt):
     (16, 128, 256, 2, 0.0, "f32"),
     (512, 1000, 640, 3, 6.0, "f32"),      # two full 256-row tiles, 112-wide column tiles, ragged n
     (16, 28688, 256, 2, 6.0, "f16"),      # 128-wide column tiles (112 would need a second round)
+    (256, 224, 8192, 40, 6.0, "f32"),     # 64 K steps: outlier weights copied from the stream
+    (8, 200, 8320, 3, 6.0, "f16"),        # 65 K steps: outlier weights gathered instead
 ])
 def test_decomp_parity(m, n, k, n_out, thr, ydt):
     say(f"int8_decomp m={m} n={n} k={k} outliers={n_out} thr={thr} y={ydt}")

@@ -159,6 +159,7 @@ def test_linear_gemm_parity(m, n, k, xdt, ydt):
 
 @pytest.mark.parametrize("m,n,k,xdt,ydt", [
     (1, 300, 1152, "f16", "f32"),     # ragged n, odd G, one tile per matrix
+    (1, 11008, 4096, "f16", "f16"),   # m = 1 with the single call's schedule: bit-equal
     (3, 257, 640, "bf16", "f32"),     # bf16 activations, ragged last tile
     (4, 11008, 4096, "f16", "f16"),
     (9, 1000, 2048, "f16", "bf16"),   # one row tile per matrix, 16 staged rows

@@ -137,13 +137,12 @@ struct W4Plan {
   int cfg;       // decode configuration id (see plan_w4a16)
   int phases;    // decode: phases over K
   int grid;      // decode: workgroups
-  size_t ws;     // workspace bytes the schedule needs (0 for every schedule)
   bool szl;      // decode: scales and zero points staged in LDS
 };
 W4Plan plan_w4a16(int64_t m, const wq_weight* w);
 hipError_t launch_w4a16(const void* x, int xdt, int64_t m, const wq_weight* w,
-                        const float* levels16, void* y, int ydt, void* ws,
-                        const W4Plan& plan, hipStream_t s);
+                        const float* levels16, void* y, int ydt, const W4Plan& plan,
+                        hipStream_t s);
 // gate/up pair sharing x (INT4, same n and k); act 1: yg = silu(gate) * up
 W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu);
 hipError_t launch_w4a16_pair(const void* x, int xdt, int64_t m, const wq_weight* wg,

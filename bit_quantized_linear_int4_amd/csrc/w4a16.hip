@@ -1174,7 +1174,7 @@ hipError_t launch_stream_pair(const SkinnyArgs& a, const Levels& lv, const W4Pla
 
 template <int XDT, int YDT>
 hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const float* levels,
-                        void* y, void* ws, const W4Plan& p, hipStream_t s) {
+                        void* y, const W4Plan& p, hipStream_t s) {
   Levels lv;
   for (int i = 0; i < 16; ++i) lv.v[i] = levels[i];
   if (p.path == 1) {
@@ -1252,11 +1252,11 @@ hipError_t launch_pair_typed(const void* x, int64_t m, const wq_weight* wg, cons
 
 template <int XDT>
 hipError_t launch_x(const void* x, int64_t m, const wq_weight* w, const float* levels, void* y,
-                    int ydt, void* ws, const W4Plan& p, hipStream_t s) {
+                    int ydt, const W4Plan& p, hipStream_t s) {
   switch (ydt) {
-    case WQ_F32: return launch_typed<XDT, WQ_F32>(x, m, w, levels, y, ws, p, s);
-    case WQ_BF16: return launch_typed<XDT, WQ_BF16>(x, m, w, levels, y, ws, p, s);
-    default: return launch_typed<XDT, WQ_F16>(x, m, w, levels, y, ws, p, s);
+    case WQ_F32: return launch_typed<XDT, WQ_F32>(x, m, w, levels, y, p, s);
+    case WQ_BF16: return launch_typed<XDT, WQ_BF16>(x, m, w, levels, y, p, s);
+    default: return launch_typed<XDT, WQ_F16>(x, m, w, levels, y, p, s);
   }
 }
 
@@ -1277,7 +1277,6 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   p.cfg = 0;
   p.phases = 1;
   p.grid = 0;
-  p.ws = 0;
   const int64_t GS = int4_groups(w);
   p.szl = w->fmt == WQ_FMT_INT4_ASYM && ((uintptr_t)w->scales % 16) == 0 &&
           ((uintptr_t)w->zeros % 16) == 0 && (w->n * GS * 2) % 16 == 0 &&
@@ -1330,10 +1329,10 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
 }
 
 hipError_t launch_w4a16(const void* x, int xdt, int64_t m, const wq_weight* w,
-                        const float* levels16, void* y, int ydt, void* ws, const W4Plan& plan,
+                        const float* levels16, void* y, int ydt, const W4Plan& plan,
                         hipStream_t s) {
-  if (xdt == WQ_BF16) return launch_x<WQ_BF16>(x, m, w, levels16, y, ydt, ws, plan, s);
-  return launch_x<WQ_F16>(x, m, w, levels16, y, ydt, ws, plan, s);
+  if (xdt == WQ_BF16) return launch_x<WQ_BF16>(x, m, w, levels16, y, ydt, plan, s);
+  return launch_x<WQ_F16>(x, m, w, levels16, y, ydt, plan, s);
 }
 
 W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
@@ -1369,7 +1368,6 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
       p.mp = pc.mp;
       p.phases = (int)((G + pc.nw * pc.gpp - 1) / (pc.nw * pc.gpp));
       p.grid = (int)((ntiles + pc.tpg / 2 - 1) / (pc.tpg / 2));
-      p.ws = 0;
       const int64_t GSp = int4_groups(wg);
       if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true,
                                     WQ_FMT_INT4_ASYM, (int)GSp, (int)((GSp + 1) / 2),
@@ -1386,9 +1384,9 @@ hipError_t launch_w4a16_pair(const void* x, int xdt, int64_t m, const wq_weight*
     // prefill: two GEMMs (the pair gains nothing once the weights are reused
     // across many rows)
     const float* lv = nf4_levels();
-    hipError_t e = launch_w4a16(x, xdt, m, wg, lv, yg, ydt, nullptr, plan, s);
+    hipError_t e = launch_w4a16(x, xdt, m, wg, lv, yg, ydt, plan, s);
     if (e != hipSuccess) return e;
-    return launch_w4a16(x, xdt, m, wu, lv, yu, ydt, nullptr, plan_w4a16(m, wu), s);
+    return launch_w4a16(x, xdt, m, wu, lv, yu, ydt, plan_w4a16(m, wu), s);
   }
 #define WQ_PAIR_Y(XDT)                                                                      \
   switch (ydt) {                                                                            \

@@ -69,11 +69,11 @@ wq_status check_weight(const wq_weight* w, bool linear_w4) {
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Workspace of wq_linear_w4a16: what the schedule needs (none today), then (act-order)
-// the gathered activations.
-size_t linear_ws_bytes(size_t plan_ws, int64_t m, const wq_weight* w) {
-  if (w->perm == nullptr) return plan_ws;
-  return round256(plan_ws) + round256((size_t)m * (size_t)w->k * 2);
+// Workspace of wq_linear_w4a16: the activations gathered into the order of
+// an act-order weight (m x k 16-bit values); none for any other weight.
+size_t linear_ws_bytes(int64_t m, const wq_weight* w) {
+  if (w->perm == nullptr) return 0;
+  return round256((size_t)m * (size_t)w->k * 2);
 }
 
 // FP4 weights run the NF4 kernels with the FP4 level table.
@@ -180,8 +180,7 @@ wq_status wq_pack_fp4(const void* w, int32_t wdt, int64_t n, int64_t k, int32_t 
 
 size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w) {
   if (m < 1 || m >= kMaxDim || check_weight(w, true) != WQ_OK) return 0;
-  const wq_weight kv = kernel_view(w);
-  return linear_ws_bytes(plan_w4a16(m, &kv).ws, m, w);
+  return linear_ws_bytes(m, w);
 }
 
 wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight* w, void* y,
@@ -196,7 +195,7 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight
   if (!aligned(x, 16) || !aligned(y, dt_bytes(ydt))) return WQ_ERR_ALIGN;
   const wq_weight kv = kernel_view(w);
   const W4Plan plan = plan_w4a16(m, &kv);
-  const size_t need = linear_ws_bytes(plan.ws, m, w);
+  const size_t need = linear_ws_bytes(m, w);
   if (need > 0) {
     if (workspace == nullptr || ws_bytes < need) return WQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return WQ_ERR_ALIGN;
@@ -204,13 +203,13 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m, const wq_weight
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w->perm != nullptr) {
     // act-order: x[:, perm] into the workspace, then the plain linear on it
-    void* xp = static_cast<char*>(workspace) + round256(plan.ws);
+    void* xp = workspace;
     const hipError_t e = launch_permute_cols(static_cast<const uint16_t*>(x), m, w->k, w->perm,
                                              static_cast<uint16_t*>(xp), s);
     if (e != hipSuccess) return WQ_ERR_HIP;
     x = xp;
   }
-  return hip_status(launch_w4a16(x, xdt, m, &kv, levels_for(w), y, ydt, workspace, plan, s));
+  return hip_status(launch_w4a16(x, xdt, m, &kv, levels_for(w), y, ydt, plan, s));
 }
 
 wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,

@@ -195,10 +195,10 @@ wq_status wq_fp4_codebook(float* out);
 wq_status wq_nf4_codebook(float* out);
 
 /*
- * Scratch bytes wq_linear_w4a16 needs for this (m, weight) pair: 0 when the
- * chosen schedule needs none; an act-order weight needs m * k * 2 bytes
- * (rounded up to 256) for the gathered activations.  Returns 0 for invalid arguments as well (the
- * call itself then reports the error).
+ * Scratch bytes wq_linear_w4a16 needs for this (m, weight) pair: an
+ * act-order weight needs m * k * 2 bytes (rounded up to 256) for the
+ * gathered activations; every other weight needs none (0).  Returns 0 for
+ * invalid arguments as well (the call itself then reports the error).
  */
 size_t wq_linear_w4a16_workspace(int64_t m, const wq_weight* w);
 

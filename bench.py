@@ -616,11 +616,14 @@ def summarize_trace(prof_dir, bench_json, title, out_path, command):
     import csv
     import statistics
     per = {}
+    order = []   # (start, key, duration) of every dispatch
     for r in csv.DictReader(open(os.path.join(prof_dir, "run_kernel_trace.csv"))):
         grid = tuple(int(r[f"Grid_Size_{a}"]) // max(1, int(r[f"Workgroup_Size_{a}"]))
                      for a in "XYZ")
         dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         per.setdefault((r["Kernel_Name"], grid), []).append(dur)
+        order.append((int(r["Start_Timestamp"]), (r["Kernel_Name"], grid), dur))
+    order.sort()
     total = sum(sum(v) for v in per.values())
     rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
     with open(out_path, "w") as f:
@@ -639,6 +642,17 @@ def summarize_trace(prof_dir, bench_json, title, out_path, command):
             f.write(f"#   value {d['value']} {d['unit']}, ms_per_step {d['ms_per_step']}, "
                     f"dominant kernel avg_launch_us {rf.get('avg_launch_us')} "
                     f"({rf.get('kernel')})\n")
+            # bench.py times the dominant kernel last, in a region of its own:
+            # the last `launches` dispatches of the last kernel shape traced
+            n = int(rf.get("launches") or 0)
+            work = [o for o in order if "copy" not in o[1][0].lower()
+                    and "elementwise" not in o[1][0]]
+            if n > 0 and work:
+                key = work[-1][1]
+                tail = [o[2] for o in work if o[1] == key][-n:]
+                f.write(f"# traced average of that region ({len(tail)} dispatches of "
+                        f"{key[0][:60]}..., {key[1]}): {statistics.mean(tail):.1f} ns; the "
+                        "table's average also holds the warmup and the full steps\n")
     print(open(out_path).read())
 
 

@@ -26,8 +26,9 @@ codes + scales + zero points + x + y, each read or written once) / step time
 
 Other workloads (--workload), one per line: decode_m1, prefill, mlp_decode
 (M = 16 through gate + up as one pair call and down [4096 x 11008]),
-nf4_m1 / nf4_m512 (NF4 14336 x 4096, bf16), int8_70b (LLM.int8 at
-28672 x 8192, M = 256).
+decode_m1_actorder (the M = 1 layer quantized in a synthetic act-order: each
+call gathers x into that order first), nf4_m1 / nf4_m512 (NF4 14336 x 4096,
+bf16), int8_70b (LLM.int8 at 28672 x 8192, M = 256).
 """
 
 import argparse
@@ -91,6 +92,8 @@ class W4Layers(Workload):
     A gate projection followed by an up projection of the same input runs
     as one pair call (the activations are read once for both)."""
 
+    act_order = None   # seed of a synthetic act-order for every layer, or None
+
     def setup(self):
         import torch
         import bit_quantized_linear_int4_amd as wq
@@ -98,14 +101,28 @@ class W4Layers(Workload):
         base, self.xs, self.ys, self.wss = [], [], [], []
         bytes_, flops = [], []
         for _, x, w in self.layers_np:
-            qw = _int4_weight(wq, torch, w)
+            if self.act_order is None:
+                qw = _int4_weight(wq, torch, w)
+            else:
+                # columns stored in quantization order; every call gathers x
+                import workloads
+                perm = torch.from_numpy(workloads.act_order_perm(w.shape[1], self.act_order)).cuda()
+                wp = torch.empty(w.shape, dtype=torch.float16, device="cuda")
+                wq.wq_permute_columns(torch.from_numpy(w).cuda(), perm, wp)
+                n, k = w.shape
+                qw = wq.alloc_int4(n, k)
+                wq.wq_quantize_groupwise(wp, 4, 128, 0, qw.codes, qw.scales, qw.zeros)
+                qw.perm = perm
+                del wp
             base.append(qw)
             m, n, k = x.shape[0], w.shape[0], w.shape[1]
             self.xs.append(torch.from_numpy(x).cuda())
             self.ys.append(torch.empty((m, n), dtype=torch.float16, device="cuda"))
-            bytes_.append(qw.nbytes() + x.size * 2 + m * n * 2)
+            # (an act-order weight also reads its permutation, 4 bytes a channel)
+            bytes_.append(qw.nbytes() + (4 * k if qw.perm is not None else 0) + x.size * 2
+                          + m * n * 2)
             flops.append(2 * m * n * k)
-            # workspace the plan asks for (act-order gathers only; none here)
+            # the workspace the call needs: act-order's gathered x, else none
             need = wq.wq_linear_w4a16_workspace(m, qw)
             self.wss.append(torch.empty((need,), dtype=torch.uint8, device="cuda") if need else None)
         torch.cuda.synchronize()
@@ -141,7 +158,8 @@ class W4Layers(Workload):
         names_dom = "/".join("+".join(self.layers_np[j][0] for j in self.units[ui])
                              for ui in self.dom)
         pair = " pair" if len(u0) == 2 else ""
-        self.kernel_desc = f"w4a16 {fam}{pair} ({names_dom}: M={m}, N={n}, K={k})"
+        act = ", act-order: x gathered first" if self.act_order is not None else ""
+        self.kernel_desc = f"w4a16 {fam}{pair} ({names_dom}: M={m}, N={n}, K={k}{act})"
 
     def _call(self, copy, ui):
         wq, ws = self.wq, self.copies[copy % len(self.copies)]
@@ -198,7 +216,9 @@ class W4Layers(Workload):
         return {"workload": self.name,
                 "layers": [{"name": nm, "m": int(x.shape[0]), "n": int(w.shape[0]),
                             "k": int(w.shape[1])} for nm, x, w in self.layers_np],
-                "format": "INT4 asymmetric, group 128, fp16 scale, 4-bit zero",
+                "format": "INT4 asymmetric, group 128, fp16 scale, 4-bit zero"
+                          + (", act-order (seeded synthetic channel order)"
+                             if self.act_order is not None else ""),
                 "calls": ["+".join(self.layers_np[j][0] for j in u) for u in self.units],
                 "weight_copies": len(self.copies)}
 
@@ -340,6 +360,11 @@ def make_workload(name):
     if name == "decode_m1":
         d = workloads.decode_m1()
         return W4Layers("decode_m1_4096x4096", [("proj", d["x"], d["w"])], "GB/s")
+    if name == "decode_m1_actorder":
+        d = workloads.decode_m1()
+        wl = W4Layers("decode_m1_actorder_4096x4096", [("proj", d["x"], d["w"])], "GB/s")
+        wl.act_order = workloads.SEEDS["decode_m1"]
+        return wl
     if name == "prefill":
         return W4Layers("prefill_m2048_7b", workloads.prefill(), "TFLOP/s")
     if name in ("nf4_m1", "nf4_m512"):
@@ -707,8 +732,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="metric",
-                    choices=["metric", "mlp_decode", "decode_m1", "prefill", "nf4_m1", "nf4_m512",
-                             "int8_70b"],
+                    choices=["metric", "mlp_decode", "decode_m1", "decode_m1_actorder", "prefill",
+                             "nf4_m1", "nf4_m512", "int8_70b"],
                     help="metric (default): the M = 1 decode layer as the value, with the "
                          "M = 2048 prefill step as the secondary figure in the same line")
     ap.add_argument("--no-cpu-baseline", action="store_true")

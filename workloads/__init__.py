@@ -28,6 +28,9 @@ synthetic layers stand in for the 7B / 8B / 70B layers they discuss):
                 [512 x 4096] ~ N(0, 1).
   int8_70b      W fp16 [28672 x 8192] ~ N(0, 0.02); x fp16 [256 x 8192]
                 ~ N(0, 1) with 8 fixed outlier channels, |x| ~ U[20, 100].
+  act_order_perm  a synthetic act-order over k input channels: the channels
+                by decreasing seeded U[0, 1) importance (choosing the real
+                order needs calibration data).
 """
 
 import numpy as np
@@ -120,3 +123,10 @@ def int8_70b(m=256, n=28672, k=8192, n_outliers=8, seed=SEEDS["int8_70b"]):
     """LLM.int8 layer: fp16 W, fp16 x with fixed outlier channels."""
     x, chans = activations(m, k, seed, 0, outliers=(n_outliers, 20.0, 100.0))
     return {"x": x, "w": weights(n, k, seed, 1), "outlier_channels": chans}
+
+
+def act_order_perm(k, seed, tid=7):
+    """A synthetic act-order: the k channels by decreasing seeded importance
+    (int32 [k], a permutation)."""
+    imp = _rng(seed, tid).random(k)
+    return np.argsort(-imp, kind="stable").astype(np.int32)

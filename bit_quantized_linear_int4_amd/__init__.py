@@ -30,7 +30,9 @@ F16, BF16, F32 = 0, 1, 2
 FMT_INT4_ASYM, FMT_NF4, FMT_INT8_SYM_ROW, FMT_FP4 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libwq.so")
+# WQ_LIBRARY names another build of the same library (for example one whose
+# host code carries sanitizers); by default the in-tree libwq.so
+_LIB_PATH = os.environ.get("WQ_LIBRARY") or os.path.join(_HERE, "libwq.so")
 _lib = None
 
 

@@ -110,8 +110,8 @@ def oracle_linear(x_np, w_np, xdt, rows=None, group=128):
 
 
 @pytest.mark.parametrize("m,n,k,xdt,ydt", [
-    (1, 300, 1152, "f16", "f32"),     # ragged n, odd G, single split
-    (1, 4096, 4096, "f16", "f32"),    # full single-layer decode shape (split-K)
+    (1, 300, 1152, "f16", "f32"),     # ragged n, odd G (9 groups over 16 waves)
+    (1, 4096, 4096, "f16", "f32"),    # full single-layer decode shape (sixteen waves)
     (1, 4096, 4096, "f16", "f16"),
     (1, 1000, 2048, "bf16", "bf16"),  # sixteen-wave m = 1 schedule, bf16 (exact decoder)
     (3, 257, 640, "bf16", "f32"),
@@ -125,7 +125,7 @@ def oracle_linear(x_np, w_np, xdt, rows=None, group=128):
     (16, 777, 1024, "bf16", "f32"),
     (1, 520, 11008, "f16", "f32"),    # three activation phases at m = 1
     (2, 300, 11008, "f16", "f16"),    # four staged rows, three phases
-    (7, 200, 13824, "f16", "f32"),    # beyond the full-K schedules: split-K path
+    (7, 200, 13824, "f16", "f32"),    # 108 groups: many phases per wave
     (16, 96, 5120, "bf16", "f32"),    # double-buffered phases, exact bf16 dequant
 ])
 def test_linear_skinny_parity(m, n, k, xdt, ydt):
@@ -146,6 +146,7 @@ def test_linear_skinny_parity(m, n, k, xdt, ydt):
     (130, 272, 1024, "f16", "f32"),   # staged-scale GEMM: ragged m and n tiles
     (40, 4096, 4096, "f16", "bf16"),  # one partial m tile, full n tiles
     (300, 11008, 4096, "f16", "f32"), # the up-projection rows, three m tiles
+    (64, 520, 11008, "f16", "f32"),   # 86 groups, past the staged GEMM's 64: the generic GEMM
 ])
 def test_linear_gemm_parity(m, n, k, xdt, ydt):
     say(f"linear_gemm m={m} n={n} k={k} x={xdt} y={ydt}")

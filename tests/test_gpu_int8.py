@@ -91,7 +91,7 @@ def test_decomp_parity(m, n, k, n_out, thr, ydt):
     say(f"  max-rel {rel:.2e}")
 
 
-def test_decomp_70b_shape_sampled():
+def test_decomp_70b_shape_sampled(record_margin):
     """The 70B layer at full size: 28672 x 8192 int8 weights, 256 tokens with
     8 outlier channels; int32 accumulators and outputs of 2048 sampled output
     features against the oracle."""
@@ -106,6 +106,7 @@ def test_decomp_70b_shape_sampled():
     assert np.array_equal(acc[:, cols], acc_ref)
     rel = check_close(y[:, cols], y_ref, "f32")
     say(f"  max-rel {rel:.2e}")
+    record_margin("LLM.int8 70B layer M=256 (2048 columns sampled)", rel)
 
 
 # ---------------------------------------------------- SmoothQuant-style W8A8

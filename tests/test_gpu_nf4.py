@@ -111,7 +111,7 @@ def test_linear_nf4_parity(m, n, k, xdt, ydt, dq):
     say(f"  max-rel {rel:.2e}")
 
 
-def test_linear_nf4_full_layer():
+def test_linear_nf4_full_layer(record_margin):
     """The 8B-shaped layer (14336 x 4096) at M = 1 (all outputs) and M = 512
     (32 sampled rows), fp32 output."""
     say("linear_nf4_full n=14336 k=4096")
@@ -123,6 +123,8 @@ def test_linear_nf4_full_layer():
         ref = oracle_y(d["x"][m], d["w"], "bf16", True, rows)
         rel = check_close(y if rows is None else y[rows], ref, "f32")
         say(f"  m={m} max-rel {rel:.2e}")
+        record_margin(f"NF4 14336x4096 M={m}" + ("" if rows is None else " (32 rows sampled)"),
+                      rel)
 
 
 # ---------------------------------------------------------------- FP4 (E2M1)

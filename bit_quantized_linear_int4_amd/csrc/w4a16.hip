@@ -127,11 +127,12 @@ struct SkinnyArgs {
   int m, n, k, G, zb;        // G = k/128 units of 128; zb = bytes per row of zeros
   int GS, sub;               // INT4: groups per row (k/group), groups per unit (1, 2, 4)
   void* y;
-  // second INT4 matrix of a gate/up pair (same n, k; same x), its output,
-  // and the epilogue: 0 = both outputs, 1 = y = silu(gate) * up only
+  // second matrix of a gate/up pair (same format, n, k; same x), its
+  // output, and the epilogue: 0 = both outputs, 1 = y = silu(gate) * up only
   const uint32_t* codes_b;
   const void* scales_b;
   const uint8_t* zeros_b;
+  const float* scales2_b;
   void* y_b;
   int act;
 };
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // DUAL: TPG counts the tiles of both matrices; tile t < TH is row tile t
   // of the first (gate) matrix, tile TH + t the same rows of the second (up)
   constexpr int TH = DUAL ? TPG / 2 : TPG;                 // row tiles per workgroup
-  static_assert(!DUAL || (TPG % 2 == 0 && FMT == WQ_FMT_INT4_ASYM), "pairs are INT4");
+  static_assert(!DUAL || TPG % 2 == 0, "a pair holds the same tiles of both matrices");
   // codes through a per-wave LDS ring (with staged scales), else in
   // registers; pairs with 16 staged rows keep them in registers (15.2
   // against 15.8 us through LDS for the 11008-row pair at M = 16, while at
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
       for (int i = tid; i < TPG * NC2; i += NW * 64) {
         const int t = i / NC2, j = i % NC2;
         const int64_t c0 = ((int64_t)tile_of(t) * 16 * bpr) >> 8;
-        c2l[t * (ZCB / 4) + j] = a.scales2[min(c0 + j, n2 - 1)];
+        c2l[t * (ZCB / 4) + j] = (second(t) ? a.scales2_b : a.scales2)[min(c0 + j, n2 - 1)];
       }
     }
     __syncthreads();   // before any direct load is in flight: costs no wait
@@ -370,8 +371,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   const uint4_t* q4a = reinterpret_cast<const uint4_t*>(a.codes);
   const uint4_t* q4b = reinterpret_cast<const uint4_t*>(DUAL ? a.codes_b : a.codes);
   const int k32 = a.k / 32;
-  const bool dq = a.scales2 != nullptr;
-  const float* s2p = dq ? a.scales2 : static_cast<const float*>(a.scales);
+  const bool dq = a.scales2 != nullptr;   // both matrices of a pair alike
   uint4_t wv[NBUF][TPG][GPP];
   float sv[NBUF][TPG][GPP];
   uint32_t zv[NBUF][TPG][GPP];
@@ -407,9 +407,12 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
           // the first-level absmax (int8 code or fp32) and the second-level
           // scale (a harmless reload of element 0 without double quantization)
           const int64_t blk = (int64_t)row * (a.k / 64) + 2 * g + (kq >> 1);
+          const void* s1p = second(t) ? a.scales_b : a.scales;
+          const float* s2p = dq ? (second(t) ? a.scales2_b : a.scales2)
+                                : static_cast<const float*>(s1p);
           const float l2 = s2p[dq ? (blk >> 8) : 0];
-          const float l1 = dq ? (float)static_cast<const int8_t*>(a.scales)[blk]
-                              : static_cast<const float*>(a.scales)[blk];
+          const float l1 = dq ? (float)static_cast<const int8_t*>(s1p)[blk]
+                              : static_cast<const float*>(s1p)[blk];
           sv[b][t][u] = dq ? l1 * l2 : l1;
           zv[b][t][u] = 0;
         }
@@ -1142,18 +1145,19 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
 }
 
 // Gate/up pair configurations: NW, TPG (tiles of both matrices), GPP, MP, NBUF.
-template <int XDT, int YDT>
+template <int FMT, int XDT, int YDT>
 hipError_t launch_stream_pair(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
                               hipStream_t s) {
 #define WQ_PAIR_T(NW, TPG, GPP, MP, NBUF, SG)                                                  \
   if (p.szl)                                                                                  \
-    return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, true, true, SG>( \
-        a, lv, p, s);                                                                         \
-  return launch_stream_t<XDT, YDT, WQ_FMT_INT4_ASYM, NW, TPG, GPP, MP, NBUF, false, true, SG>(  \
-      a, lv, p, s);
+    return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, true, true, SG>(a, lv, p, s); \
+  /* NF4 absmax loaded per unit with eight tiles would spill: never planned */                \
+  if constexpr (FMT == WQ_FMT_NF4 && TPG >= 8) return hipErrorInvalidConfiguration;           \
+  else                                                                                        \
+    return launch_stream_t<XDT, YDT, FMT, NW, TPG, GPP, MP, NBUF, false, true, SG>(a, lv, p, s);
 #define WQ_PAIR(C, NW, TPG, GPP, MP, NBUF)                                                    \
   case C:                                                                                     \
-    if constexpr (XDT == WQ_F16) {                                                            \
+    if constexpr (FMT == WQ_FMT_INT4_ASYM && XDT == WQ_F16) {                                 \
       if (a.sub > 1) {                                                                        \
         WQ_PAIR_T(NW, TPG, GPP, MP, NBUF, true)                                               \
       }                                                                                       \
@@ -1227,13 +1231,16 @@ hipError_t launch_typed(const void* x, int64_t m, const wq_weight* w, const floa
 
 template <int XDT, int YDT>
 hipError_t launch_pair_typed(const void* x, int64_t m, const wq_weight* wg, const wq_weight* wu,
-                             int act, void* yg, void* yu, const W4Plan& p, hipStream_t s) {
+                             const float* levels, int act, void* yg, void* yu, const W4Plan& p,
+                             hipStream_t s) {
   Levels lv{};
+  for (int i = 0; i < 16; ++i) lv.v[i] = levels[i];
   SkinnyArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.codes = static_cast<const uint32_t*>(wg->codes);
   a.scales = wg->scales;
   a.zeros = wg->zeros;
+  a.scales2 = wg->scales2;
   a.m = (int)m;
   a.n = (int)wg->n;
   a.k = (int)wg->k;
@@ -1245,9 +1252,11 @@ hipError_t launch_pair_typed(const void* x, int64_t m, const wq_weight* wg, cons
   a.codes_b = static_cast<const uint32_t*>(wu->codes);
   a.scales_b = wu->scales;
   a.zeros_b = wu->zeros;
+  a.scales2_b = wu->scales2;
   a.y_b = yu;
   a.act = act;
-  return launch_stream_pair<XDT, YDT>(a, lv, p, s);
+  if (wg->fmt == WQ_FMT_NF4) return launch_stream_pair<WQ_FMT_NF4, XDT, YDT>(a, lv, p, s);
+  return launch_stream_pair<WQ_FMT_INT4_ASYM, XDT, YDT>(a, lv, p, s);
 }
 
 template <int XDT>
@@ -1360,39 +1369,49 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
     const int64_t th = (ntiles + 255) / 256;
     cfg = th >= 4 ? 65 : th == 3 ? 67 : (th == 2 ? 63 : 62);
   }
-  for (const PCfg& pc : pcfgs)
-    if (pc.id == cfg) {
-      p.cfg = pc.id;
-      p.tpg = pc.tpg;
-      p.gpw = pc.gpp;
-      p.mp = pc.mp;
-      p.phases = (int)((G + pc.nw * pc.gpp - 1) / (pc.nw * pc.gpp));
-      p.grid = (int)((ntiles + pc.tpg / 2 - 1) / (pc.tpg / 2));
-      const int64_t GSp = int4_groups(wg);
-      if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true,
-                                    WQ_FMT_INT4_ASYM, (int)GSp, (int)((GSp + 1) / 2),
-                                    (int)wg->k) > 160 * 1024 - 256)
-        p.szl = false;
-    }
+  const bool szl0 = p.szl;
+  auto apply = [&](int id) {
+    p.szl = szl0;
+    for (const PCfg& pc : pcfgs)
+      if (pc.id == id) {
+        p.cfg = pc.id;
+        p.tpg = pc.tpg;
+        p.gpw = pc.gpp;
+        p.mp = pc.mp;
+        p.phases = (int)((G + pc.nw * pc.gpp - 1) / (pc.nw * pc.gpp));
+        p.grid = (int)((ntiles + pc.tpg / 2 - 1) / (pc.tpg / 2));
+        const int64_t GSp = int4_groups(wg);
+        if (p.szl && stream_lds_bytes(pc.nw, pc.tpg, pc.gpp, pc.mp, pc.nbuf, true, true,
+                                      wg->fmt, (int)GSp, (int)((GSp + 1) / 2),
+                                      (int)wg->k) > 160 * 1024 - 256)
+          p.szl = false;
+      }
+  };
+  apply(cfg);
+  // NF4/FP4 whose absmax is not staged: four tiles of each matrix would hold
+  // too many registers (their absmax is loaded per unit); two instead
+  if (p.cfg == 65 && wg->fmt == WQ_FMT_NF4 && !p.szl) apply(63);
   return p;
 }
 
 hipError_t launch_w4a16_pair(const void* x, int xdt, int64_t m, const wq_weight* wg,
-                             const wq_weight* wu, int act, void* yg, void* yu, int ydt,
-                             const W4Plan& plan, hipStream_t s) {
+                             const wq_weight* wu, const float* levels16, int act, void* yg,
+                             void* yu, int ydt, const W4Plan& plan, hipStream_t s) {
   if (plan.path == 1) {
     // prefill: two GEMMs (the pair gains nothing once the weights are reused
     // across many rows)
-    const float* lv = nf4_levels();
-    hipError_t e = launch_w4a16(x, xdt, m, wg, lv, yg, ydt, plan, s);
+    hipError_t e = launch_w4a16(x, xdt, m, wg, levels16, yg, ydt, plan, s);
     if (e != hipSuccess) return e;
-    return launch_w4a16(x, xdt, m, wu, lv, yu, ydt, plan_w4a16(m, wu), s);
+    return launch_w4a16(x, xdt, m, wu, levels16, yu, ydt, plan_w4a16(m, wu), s);
   }
 #define WQ_PAIR_Y(XDT)                                                                      \
   switch (ydt) {                                                                            \
-    case WQ_F32: return launch_pair_typed<XDT, WQ_F32>(x, m, wg, wu, act, yg, yu, plan, s);   \
-    case WQ_BF16: return launch_pair_typed<XDT, WQ_BF16>(x, m, wg, wu, act, yg, yu, plan, s); \
-    default: return launch_pair_typed<XDT, WQ_F16>(x, m, wg, wu, act, yg, yu, plan, s);       \
+    case WQ_F32:                                                                            \
+      return launch_pair_typed<XDT, WQ_F32>(x, m, wg, wu, levels16, act, yg, yu, plan, s);  \
+    case WQ_BF16:                                                                           \
+      return launch_pair_typed<XDT, WQ_BF16>(x, m, wg, wu, levels16, act, yg, yu, plan, s); \
+    default:                                                                                \
+      return launch_pair_typed<XDT, WQ_F16>(x, m, wg, wu, levels16, act, yg, yu, plan, s);  \
   }
   if (xdt == WQ_BF16) {
     WQ_PAIR_Y(WQ_BF16)

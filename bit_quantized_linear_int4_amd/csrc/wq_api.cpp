@@ -222,7 +222,12 @@ wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
   if (st != WQ_OK) return st;
   st = check_weight(w_up, true);
   if (st != WQ_OK) return st;
-  if (w_gate->fmt != WQ_FMT_INT4_ASYM || w_up->fmt != WQ_FMT_INT4_ASYM) return WQ_ERR_UNSUPPORTED;
+  // both matrices in one format (INT4, NF4 or FP4), NF4/FP4 both with or both
+  // without double quantization
+  if (w_gate->fmt != w_up->fmt || w_gate->fmt == WQ_FMT_INT8_SYM_ROW) return WQ_ERR_UNSUPPORTED;
+  if ((w_gate->scales2 == nullptr) != (w_up->scales2 == nullptr) ||
+      (w_gate->scales2 != nullptr && w_gate->group2 != w_up->group2))
+    return WQ_ERR_UNSUPPORTED;
   if (w_gate->perm != nullptr || w_up->perm != nullptr) return WQ_ERR_UNSUPPORTED;
   if (!is16(xdt) || !is_out(ydt)) return WQ_ERR_UNSUPPORTED;
   if (w_gate->n != w_up->n || w_gate->k != w_up->k || w_gate->group != w_up->group ||
@@ -234,8 +239,9 @@ wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
   if (!aligned(x, 16) || !aligned(y_gate, dt_bytes(ydt)) ||
       (act == 0 && !aligned(y_up, dt_bytes(ydt))))
     return WQ_ERR_ALIGN;
-  const W4Plan plan = plan_w4a16_pair(m, w_gate, w_up);
-  return hip_status(launch_w4a16_pair(x, xdt, m, w_gate, w_up, act, y_gate,
+  const wq_weight kg = kernel_view(w_gate), ku = kernel_view(w_up);
+  const W4Plan plan = plan_w4a16_pair(m, &kg, &ku);
+  return hip_status(launch_w4a16_pair(x, xdt, m, &kg, &ku, levels_for(w_gate), act, y_gate,
                                       act == 0 ? y_up : nullptr, ydt, plan,
                                       static_cast<hipStream_t>(stream)));
 }

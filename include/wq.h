@@ -238,12 +238,15 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m,
  * For m <= 16 one pass streams both matrices with the activations staged
  * once; larger m runs the two GEMMs (act = 1 is decode only).
  *
- * x: xdt in {WQ_F16, WQ_BF16}, [m][k], 16-byte aligned.  w_gate, w_up:
- * INT4_ASYM (group 128, 64 or 32) with equal n and k.  y_gate, y_up: ydt in
- * {F16, BF16, F32}, [m][n] each (y_up may be NULL when act = 1).
- * Errors: WQ_ERR_SHAPE when n, k or the group size differ; WQ_ERR_UNSUPPORTED for NF4,
- * act-order weights, act outside {0, 1}, or act = 1 with m > 16.  No
- * workspace.
+ * x: xdt in {WQ_F16, WQ_BF16}, [m][k], 16-byte aligned.  w_gate, w_up: one
+ * format for both -- INT4_ASYM (group 128, 64 or 32), NF4 or FP4 (block 64,
+ * both with or both without double quantization) -- with equal n and k.
+ * y_gate, y_up: ydt in {F16, BF16, F32}, [m][n] each (y_up may be NULL when
+ * act = 1).
+ * Errors: WQ_ERR_SHAPE when n, k or the group size differ;
+ * WQ_ERR_UNSUPPORTED for mixed formats, INT8 weights, NF4/FP4 with double
+ * quantization on one matrix only, act-order weights, act outside {0, 1},
+ * or act = 1 with m > 16.  No workspace.
  */
 wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
                                   const wq_weight* w_gate, const wq_weight* w_up,

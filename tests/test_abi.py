@@ -185,7 +185,12 @@ def test_gate_up_argument_errors():
     assert call(wu=_weight(group=64)) == SHAPE        # and the group size
     assert call(m=0) == SHAPE
     assert call(m=1 << 23) == SHAPE
-    assert call(wg=_weight(fmt=wq.FMT_NF4, group=64, zeros=None)) == UNSUP
+    assert call(wg=_weight(fmt=wq.FMT_NF4, group=64, zeros=None)) == UNSUP   # mixed formats
+    nf4 = dict(fmt=wq.FMT_NF4, group=64, zeros=None)
+    assert call(wg=_weight(**nf4, scales2=A16, group2=256),
+                wu=_weight(**nf4)) == UNSUP           # double quantization on one only
+    int8 = dict(fmt=wq.FMT_INT8_SYM_ROW, group=256, zeros=None)
+    assert call(wg=_weight(**int8), wu=_weight(**int8)) == UNSUP
     assert call(xdt=wq.F32) == UNSUP
     assert call(x=ODD) == ALIGN
     assert call(yu=ODD, act=0) == ALIGN

@@ -193,3 +193,69 @@ def test_linear_fp4_parity(m, n, k, xdt, ydt, dq):
     wh = fp4.dequantize(c, a, c2, (n, k), out_dtype=xdt)
     rel = check_close(to_np(y), linear.reference(host16(x, xdt), wh), ydt)
     say(f"  max-rel {rel:.2e}")
+
+
+# ------------------------------------------------ NF4 / FP4 gate/up pairs
+
+def _fmt_oracle(fmt, w, xdt, dq):
+    mod = nf4 if fmt == "nf4" else fp4
+    c, a, c2 = mod.quantize(host16(w, xdt), double_quant=dq)
+    return mod.dequantize(c, a, c2, w.shape, out_dtype=xdt)
+
+
+@pytest.mark.parametrize("fmt,m,n,k,xdt,ydt,dq", [
+    ("nf4", 1, 14336, 4096, "bf16", "f32", True),   # the 8B gate/up shape, one token
+    ("nf4", 1, 300, 1152, "bf16", "bf16", True),    # ragged n, odd unit count
+    ("nf4", 4, 1000, 2048, "bf16", "f32", True),
+    ("nf4", 16, 14336, 4096, "bf16", "f32", True),  # four tiles of each matrix
+    ("nf4", 16, 4100, 1024, "f16", "f32", False),   # fp32 absmax: loaded per unit
+    ("nf4", 16, 14336, 1024, "bf16", "f32", False), # fp32 absmax, 896 tiles: two per matrix
+    ("nf4", 40, 300, 1152, "bf16", "f32", True),    # prefill rows: two GEMMs
+    ("fp4", 1, 1000, 2048, "bf16", "f32", True),
+    ("fp4", 16, 5120, 1024, "f16", "bf16", False),
+])
+def test_gate_up_pair_nf4_fp4(fmt, m, n, k, xdt, ydt, dq):
+    """Both outputs of an NF4 / FP4 pair against the oracle, and equal bit
+    for bit to the two single-matrix calls (the pair runs the same per-tile
+    schedule)."""
+    say(f"gate_up {fmt} m={m} n={n} k={k} x={xdt} y={ydt} dq={dq}")
+    seed = 600 + m + n
+    x_np, _ = workloads.activations(m, k, seed, 0, dtype=xdt)
+    wg_np = workloads.weights(n, k, seed, 1, dtype=xdt)
+    wu_np = workloads.weights(n, k, seed, 2, dtype=xdt)
+    pack = gpu_pack if fmt == "nf4" else gpu_pack_fp4
+    qg, qu = pack(dev(wg_np, xdt), dq), pack(dev(wu_np, xdt), dq)
+    x = dev(x_np, xdt)
+    yg = torch.empty((m, n), dtype=torch_dtype(ydt), device="cuda")
+    yu = torch.empty_like(yg)
+    wq.wq_linear_w4a16_gate_up(x, qg, qu, yg, yu, act=0)
+    g1 = torch.empty_like(yg)
+    u1 = torch.empty_like(yg)
+    wq.wq_linear_w4a16(x, qg, g1, None)
+    wq.wq_linear_w4a16(x, qu, u1, None)
+    torch.cuda.synchronize()
+    xs = host16(x_np, xdt)
+    rg = check_close(to_np(yg), linear.reference(xs, _fmt_oracle(fmt, wg_np, xdt, dq)), ydt)
+    ru = check_close(to_np(yu), linear.reference(xs, _fmt_oracle(fmt, wu_np, xdt, dq)), ydt)
+    say(f"  max-rel gate {rg:.2e} up {ru:.2e}")
+    assert np.array_equal(to_np(yg), to_np(g1)) and np.array_equal(to_np(yu), to_np(u1))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 2048), (16, 5120, 1024)])
+def test_gate_up_nf4_swiglu(m, n, k):
+    """silu(gate) * up of an NF4 pair against the oracle's product of its own
+    fp64 projections."""
+    say(f"gate_up_swiglu nf4 m={m} n={n} k={k}")
+    seed = 700 + m + n
+    x_np, _ = workloads.activations(m, k, seed, 0, dtype="bf16")
+    wg_np = workloads.weights(n, k, seed, 1, dtype="bf16")
+    wu_np = workloads.weights(n, k, seed, 2, dtype="bf16")
+    qg, qu = gpu_pack(dev(wg_np, "bf16")), gpu_pack(dev(wu_np, "bf16"))
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    wq.wq_linear_w4a16_gate_up(dev(x_np, "bf16"), qg, qu, y, None, act=1)
+    torch.cuda.synchronize()
+    xs = host16(x_np, "bf16")
+    ref = linear.silu_gated(linear.reference(xs, _fmt_oracle("nf4", wg_np, "bf16", True)),
+                            linear.reference(xs, _fmt_oracle("nf4", wu_np, "bf16", True)))
+    rel = check_close(to_np(y), ref, "f32")
+    say(f"  max-rel {rel:.2e}")

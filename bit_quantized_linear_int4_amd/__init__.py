@@ -385,8 +385,11 @@ def wq_linear_w4a16(x, weight, y, workspace=None, stream=None):
 
 def wq_linear_w4a16_gate_up(x, w_gate, w_up, y_gate, y_up=None, act=0, stream=None):
     what = "wq_linear_w4a16_gate_up"
+    # y_up receives the up projection for act 0, and for act 1 once m > 16
+    # (the two-GEMM path keeps it there before the SiLU product)
+    up_out = act == 0 or x.shape[0] > 16
     _, tg = _check_linear(what, x, w_gate,
-                          [("y_gate", y_gate)] + ([("y_up", y_up)] if act == 0 else []))
+                          [("y_gate", y_gate)] + ([("y_up", y_up)] if up_out else []))
     _, tu = _check_linear(what, x, w_up, [])
     _on_gpu(what, *tg, *tu)
     dg, du = w_gate.descriptor(), w_up.descriptor()

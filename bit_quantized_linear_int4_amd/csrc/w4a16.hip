@@ -1394,15 +1394,57 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
   return p;
 }
 
+namespace {
+
+// yg = silu(yg) * yu elementwise, in fp32 on the stored values (the SiLU
+// product after the two prefill GEMMs); 8 elements per lane, the tail
+// element by element.
+template <int YDT>
+__global__ __launch_bounds__(256) void silu_mul_kernel(void* __restrict__ yg,
+                                                       const void* __restrict__ yu,
+                                                       int64_t count) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t i = i0 + j;
+    if (i >= count) return;
+    float g, u;
+    if constexpr (YDT == WQ_F32) {
+      g = static_cast<const float*>(yg)[i];
+      u = static_cast<const float*>(yu)[i];
+    } else {
+      g = load16<YDT>(static_cast<const uint16_t*>(yg) + i);
+      u = load16<YDT>(static_cast<const uint16_t*>(yu) + i);
+    }
+    store_y<YDT>(yg, i, g / (1.0f + expf(-g)) * u);
+  }
+}
+
+hipError_t launch_silu_mul(void* yg, const void* yu, int64_t count, int ydt, hipStream_t s) {
+  const dim3 grid((unsigned)((count + 2047) / 2048));
+  if (ydt == WQ_F32)
+    silu_mul_kernel<WQ_F32><<<grid, 256, 0, s>>>(yg, yu, count);
+  else if (ydt == WQ_BF16)
+    silu_mul_kernel<WQ_BF16><<<grid, 256, 0, s>>>(yg, yu, count);
+  else
+    silu_mul_kernel<WQ_F16><<<grid, 256, 0, s>>>(yg, yu, count);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_w4a16_pair(const void* x, int xdt, int64_t m, const wq_weight* wg,
                              const wq_weight* wu, const float* levels16, int act, void* yg,
                              void* yu, int ydt, const W4Plan& plan, hipStream_t s) {
   if (plan.path == 1) {
     // prefill: two GEMMs (the pair gains nothing once the weights are reused
-    // across many rows)
+    // across many rows); act 1 then forms silu(gate) * up from the two
+    // stored outputs, the up projection held in yu
     hipError_t e = launch_w4a16(x, xdt, m, wg, levels16, yg, ydt, plan, s);
     if (e != hipSuccess) return e;
-    return launch_w4a16(x, xdt, m, wu, levels16, yu, ydt, plan_w4a16(m, wu), s);
+    e = launch_w4a16(x, xdt, m, wu, levels16, yu, ydt, plan_w4a16(m, wu), s);
+    if (e != hipSuccess || act == 0) return e;
+    return launch_silu_mul(yg, yu, m * wg->n, ydt, s);
   }
 #define WQ_PAIR_Y(XDT)                                                                      \
   switch (ydt) {                                                                            \

@@ -235,14 +235,16 @@ wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
     return WQ_ERR_SHAPE;
   if (m < 1 || m >= kMaxDim || m > kMaxElems / w_gate->k || m > kMaxElems / w_gate->n)
     return WQ_ERR_SHAPE;
-  if (act == 1 && m > 16) return WQ_ERR_UNSUPPORTED;
+  // act 1 with m > 16 runs two GEMMs and needs y_up to hold the up projection
+  const bool up_out = act == 0 || m > 16;
+  if (act == 1 && m > 16 && y_up == nullptr) return WQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y_gate, dt_bytes(ydt)) ||
-      (act == 0 && !aligned(y_up, dt_bytes(ydt))))
+      (up_out && !aligned(y_up, dt_bytes(ydt))))
     return WQ_ERR_ALIGN;
   const wq_weight kg = kernel_view(w_gate), ku = kernel_view(w_up);
   const W4Plan plan = plan_w4a16_pair(m, &kg, &ku);
   return hip_status(launch_w4a16_pair(x, xdt, m, &kg, &ku, levels_for(w_gate), act, y_gate,
-                                      act == 0 ? y_up : nullptr, ydt, plan,
+                                      up_out ? y_up : nullptr, ydt, plan,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -232,21 +232,23 @@ wq_status wq_linear_w4a16(const void* x, int32_t xdt, int64_t m,
  *
  *   act = 0:  y_gate = x * W_gate_hat^T,  y_up = x * W_up_hat^T
  *             (each exactly what wq_linear_w4a16 computes for it);
- *   act = 1:  y_gate = silu(g) * u with g, u those two products in fp32
- *             and silu(v) = v / (1 + exp(-v)); y_up is not written.
+ *   act = 1:  y_gate = silu(g) * u with silu(v) = v / (1 + exp(-v)), for
+ *             m <= 16 with g, u those two products in fp32 (y_up is not
+ *             written and may be NULL); for m > 16 with g, u the two GEMM
+ *             outputs as stored in ydt (y_up is required: it receives u).
  *
  * For m <= 16 one pass streams both matrices with the activations staged
- * once; larger m runs the two GEMMs (act = 1 is decode only).
+ * once; larger m runs the two GEMMs.
  *
  * x: xdt in {WQ_F16, WQ_BF16}, [m][k], 16-byte aligned.  w_gate, w_up: one
  * format for both -- INT4_ASYM (group 128, 64 or 32), NF4 or FP4 (block 64,
  * both with or both without double quantization) -- with equal n and k.
  * y_gate, y_up: ydt in {F16, BF16, F32}, [m][n] each (y_up may be NULL when
- * act = 1).
- * Errors: WQ_ERR_SHAPE when n, k or the group size differ;
- * WQ_ERR_UNSUPPORTED for mixed formats, INT8 weights, NF4/FP4 with double
- * quantization on one matrix only, act-order weights, act outside {0, 1},
- * or act = 1 with m > 16.  No workspace.
+ * act = 1 and m <= 16).
+ * Errors: WQ_ERR_SHAPE when n, k or the group size differ; WQ_ERR_NULL when
+ * y_up is NULL for act = 0 or for act = 1 with m > 16; WQ_ERR_UNSUPPORTED
+ * for mixed formats, INT8 weights, NF4/FP4 with double quantization on one
+ * matrix only, act-order weights or act outside {0, 1}.  No workspace.
  */
 wq_status wq_linear_w4a16_gate_up(const void* x, int32_t xdt, int64_t m,
                                   const wq_weight* w_gate, const wq_weight* w_up,

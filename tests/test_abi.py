@@ -179,7 +179,9 @@ def test_gate_up_argument_errors():
     assert call(yu=None) == NULL                      # act 0 writes both outputs
     assert call(wu=_weight(zeros=None)) == NULL
     assert call(act=2) == UNSUP
-    assert call(act=1, m=17) == UNSUP                 # the SiLU product is decode only
+    assert call(act=1, m=17, yu=None) == NULL         # prefill SiLU keeps up in y_up
+    assert call(act=1, m=17, yu=ODD) == ALIGN
+    assert call(act=1, m=16, yu=ODD, x=ODD) == ALIGN  # decode: y_up unused, x checked
     assert call(wu=_weight(n=128)) == SHAPE           # the pair shares n and k
     assert call(wu=_weight(k=384)) == SHAPE
     assert call(wu=_weight(group=64)) == SHAPE        # and the group size

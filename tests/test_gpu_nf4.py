@@ -241,10 +241,11 @@ def test_gate_up_pair_nf4_fp4(fmt, m, n, k, xdt, ydt, dq):
     assert np.array_equal(to_np(yg), to_np(g1)) and np.array_equal(to_np(yu), to_np(u1))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 1000, 2048), (16, 5120, 1024)])
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 2048), (16, 5120, 1024), (96, 1000, 2048)])
 def test_gate_up_nf4_swiglu(m, n, k):
     """silu(gate) * up of an NF4 pair against the oracle's product of its own
-    fp64 projections."""
+    fp64 projections (past 16 rows the two GEMMs store fp32 gate and up, so
+    the product is still formed from fp32 sums)."""
     say(f"gate_up_swiglu nf4 m={m} n={n} k={k}")
     seed = 700 + m + n
     x_np, _ = workloads.activations(m, k, seed, 0, dtype="bf16")
@@ -252,7 +253,8 @@ def test_gate_up_nf4_swiglu(m, n, k):
     wu_np = workloads.weights(n, k, seed, 2, dtype="bf16")
     qg, qu = gpu_pack(dev(wg_np, "bf16")), gpu_pack(dev(wu_np, "bf16"))
     y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-    wq.wq_linear_w4a16_gate_up(dev(x_np, "bf16"), qg, qu, y, None, act=1)
+    yu = torch.empty_like(y) if m > 16 else None
+    wq.wq_linear_w4a16_gate_up(dev(x_np, "bf16"), qg, qu, y, yu, act=1)
     torch.cuda.synchronize()
     xs = host16(x_np, "bf16")
     ref = linear.silu_gated(linear.reference(xs, _fmt_oracle("nf4", wg_np, "bf16", True)),

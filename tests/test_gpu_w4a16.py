@@ -219,6 +219,53 @@ def test_gate_up_swiglu_parity(m, n, k, ydt):
     say(f"  max-rel {rel:.2e}")
 
 
+@pytest.mark.parametrize("m,n,k,xdt,ydt", [
+    (17, 300, 1152, "f16", "f32"),      # the first row count past the decode pass
+    (64, 520, 2048, "f16", "f16"),
+    (200, 1000, 1024, "bf16", "bf16"),  # ragged tiles, bf16 throughout
+    (512, 11008, 4096, "f16", "f16"),   # the full MLP block at prefill
+])
+def test_gate_up_swiglu_prefill(m, n, k, xdt, ydt):
+    """silu(gate) * up past 16 rows: two GEMMs store gate and up in the output
+    type, then the product is taken on those stored values.  Checked two ways:
+    within one output ulp of silu(g) * u formed in fp32 from the act 0 outputs
+    of the same call (the same GEMMs, so the same g and u), and against the
+    oracle's fp64 product.  There three roundings to the output type (g, u and
+    the result, each within 2^-9 relative in bf16 and 2^-11 in fp16, with
+    silu's relative sensitivity to g under 1.3 where silu is not small) add at
+    most 3.3 such terms: under 2^-7 |y| in bf16 and within the plain bound in
+    fp16."""
+    say(f"gate_up_swiglu prefill m={m} n={n} k={k} x={xdt} y={ydt}")
+    seed = 450 + m + n
+    x_np, _ = workloads.activations(m, k, seed, 0, dtype=xdt, outliers=(min(6, k // 128), 20.0, 80.0))
+    wg_np = workloads.weights(n, k, seed, 1, dtype=xdt)
+    wu_np = workloads.weights(n, k, seed, 2, dtype=xdt)
+    qg, qu = gpu_quantize_int4(dev(wg_np, xdt)), gpu_quantize_int4(dev(wu_np, xdt))
+    x = dev(x_np, xdt)
+    y = torch.empty((m, n), dtype=torch_dtype(ydt), device="cuda")
+    yu = torch.empty_like(y)
+    g0, u0 = torch.empty_like(y), torch.empty_like(y)
+    wq.wq_linear_w4a16_gate_up(x, qg, qu, g0, u0, act=0)
+    wq.wq_linear_w4a16_gate_up(x, qg, qu, y, yu, act=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(yu), to_np(u0)), "y_up holds the up projection"
+    g, u = to_np(g0).astype(np.float32), to_np(u0).astype(np.float32)
+    near = (g / (np.float32(1) + np.exp(-g)) * u).astype(np.float64)
+    # host and device exp differ by a few fp32 ulps; 2^-24 covers fp16 subnormals
+    ulp = {"f32": 2.0 ** -20, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[ydt]
+    got = to_np(y).astype(np.float64)
+    assert (np.abs(got - near) <= ulp * np.abs(near) + 2.0 ** -24).all()
+    ref = linear.silu_gated(oracle_linear(x_np, wg_np, xdt), oracle_linear(x_np, wu_np, xdt))
+    if ydt == "bf16":
+        den = np.abs(ref).max()
+        err = np.abs(got - ref)
+        assert (err <= 2e-3 * den + 2.0 ** -7 * np.abs(ref)).all()
+        rel = float(err.max() / den)
+    else:
+        rel = check_close(got, ref, ydt)
+    say(f"  max-rel {rel:.2e}")
+
+
 @pytest.mark.parametrize("m,n,k,xdt,ydt,group", [
     (1, 300, 1152, "f16", "f32", 64),     # scales not stageable (n * zb % 16 != 0)
     (1, 4096, 4096, "f16", "f16", 32),

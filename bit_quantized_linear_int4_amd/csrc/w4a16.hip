@@ -7,7 +7,8 @@
 // Two kernel families:
 //
 //  * stream (m <= 16, decode).  HBM-bound: the packed codes are streamed
-//    once with 16-byte loads, 16 rows x 64 bytes per wave instruction.  The
+//    once with 16-byte loads, 16 rows x 64 bytes per wave instruction (8
+//    rows x 128 bytes, whole lines, where a wave takes groups in pairs).  The
 //    multiply runs on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}) with
 //    the activations (m padded to 1, 4 or 16 staged rows) as the A operand
 //    and the codes as the B operand, so no cross-lane reduction is needed
@@ -261,6 +262,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // against 15.8 us through LDS for the 11008-row pair at M = 16, while at
   // M = 1 the ring is faster, 13.1 against 14.1 us; A/B in one run)
   constexpr bool CRING = SZL && (!DUAL || MP == 1);
+  // whole-line code loads (one staged row, groups taken in pairs): a load
+  // covers 8 rows x 128 bytes, two adjacent groups, instead of 16 rows x 64
+  // bytes, so no 128-byte line is split between two loads; lane l of load v
+  // of a pair brings chunk (l & 7) ^ lsw(r) of row r = 8 v + (l >> 3), which
+  // keeps the 16 rows an operand read gathers in different LDS banks
+  // (4096 x 11008 at M = 1: 8.06-8.18 against 8.41-8.46 us, the same bits,
+  // A/B in one run, twice)
+  constexpr bool PAIRLD = CRING && MP == 1 && GPP % 2 == 0;
   constexpr int CG = NW * GPP;                             // groups per phase
   constexpr int XS = (MP * GPP * 16 + 63) / 64 * 64;       // slots per wave buffer
   // direct activation loads per phase: 1 KB each, or with one staged row
@@ -275,6 +284,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, kq = lane >> 4;
+  auto lsw = [](int r) { return (r >> 1) & 7; };   // chunk swizzle of row r (PAIRLD)
   // INT4 group of this lane's codes: lane kq holds quarter kq (32 codes) of
   // each unit of 128, i.e. group unit * sub + lq
   const int lq = (kq * a.sub) >> 2;
@@ -386,7 +396,20 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
 #pragma unroll
       for (int u = 0; u < GPP; ++u) {
         const int g = unit(p * CG + wave * GPP + u);
-        if constexpr (CRING) {
+        if constexpr (PAIRLD) {
+          // groups u and u + 1 (u even): rows 8 v .. 8 v + 7 of the tile, 128
+          // bytes each; chunks past the row end reload its last one
+          if (u % 2 == 0) {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+              const int r = 8 * v + (lane >> 3);
+              const int rw = min(tile_of(t) * 16 + r, a.n - 1);
+              const int c = min(g * 4 + ((lane & 7) ^ lsw(r)), k32 - 1);
+              lds_dma16_nt(q4 + (int64_t)rw * k32 + c,
+                           (lds_void_t*)(wring + ((b * TPG + t) * GPP + u + v) * 64));
+            }
+          }
+        } else if constexpr (CRING) {
           // one staged activation row (M = 1): the non-temporal policy for
           // the codes (1.5-2.5% faster on the M = 1 layers, A/B in one run;
           // with 16 rows, where the activations are re-read from L2 far
@@ -474,7 +497,13 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
         if constexpr (SZL) {
 #pragma unroll
           for (int t = 0; t < TPG; ++t) {
-            if constexpr (CRING) wv[b][t][u] = wring[((b * TPG + t) * GPP + u) * 64 + lane];
+            if constexpr (PAIRLD) {
+              const int cc = (u & 1) * 4 + kq;          // chunk within the pair's 128 bytes
+              wv[b][t][u] = wring[((b * TPG + t) * GPP + (u & ~1) + (nl >> 3)) * 64 + (nl & 7) * 8 +
+                                  (cc ^ lsw(nl))];
+            } else if constexpr (CRING) {
+              wv[b][t][u] = wring[((b * TPG + t) * GPP + u) * 64 + lane];
+            }
             if constexpr (FMT == WQ_FMT_NF4) {
               // absmax of this lane's block, fp32(q8) * c2 as the double
               // quantization defines it

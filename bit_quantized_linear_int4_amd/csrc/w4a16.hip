@@ -262,14 +262,15 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // against 15.8 us through LDS for the 11008-row pair at M = 16, while at
   // M = 1 the ring is faster, 13.1 against 14.1 us; A/B in one run)
   constexpr bool CRING = SZL && (!DUAL || MP == 1);
-  // whole-line code loads (one staged row, groups taken in pairs): a load
-  // covers 8 rows x 128 bytes, two adjacent groups, instead of 16 rows x 64
+  // whole-line code loads (codes through the LDS ring, groups taken in
+  // pairs): a load covers 8 rows x 128 bytes, two adjacent groups, instead of 16 rows x 64
   // bytes, so no 128-byte line is split between two loads; lane l of load v
   // of a pair brings chunk (l & 7) ^ lsw(r) of row r = 8 v + (l >> 3), which
   // keeps the 16 rows an operand read gathers in different LDS banks
-  // (4096 x 11008 at M = 1: 8.06-8.18 against 8.41-8.46 us, the same bits,
-  // A/B in one run, twice)
-  constexpr bool PAIRLD = CRING && MP == 1 && GPP % 2 == 0;
+  // (4096 x 11008 at M = 1: 8.06-8.18 against 8.41-8.46 us, the same bits;
+  // at M = 16 with four waves 11.59-11.62 against 11.91-11.94 us for eight
+  // waves and one group per phase; A/B in one run, twice each)
+  constexpr bool PAIRLD = CRING && GPP % 2 == 0;
   constexpr int CG = NW * GPP;                             // groups per phase
   constexpr int XS = (MP * GPP * 16 + 63) / 64 * 64;       // slots per wave buffer
   // direct activation loads per phase: 1 KB each, or with one staged row
@@ -405,8 +406,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
               const int r = 8 * v + (lane >> 3);
               const int rw = min(tile_of(t) * 16 + r, a.n - 1);
               const int c = min(g * 4 + ((lane & 7) ^ lsw(r)), k32 - 1);
-              lds_dma16_nt(q4 + (int64_t)rw * k32 + c,
-                           (lds_void_t*)(wring + ((b * TPG + t) * GPP + u + v) * 64));
+              lds_void_t* dst = (lds_void_t*)(wring + ((b * TPG + t) * GPP + u + v) * 64);
+              if constexpr (MP == 1) lds_dma16_nt(q4 + (int64_t)rw * k32 + c, dst);
+              else lds_dma16(q4 + (int64_t)rw * k32 + c, dst);
             }
           }
         } else if constexpr (CRING) {
@@ -1167,6 +1169,7 @@ hipError_t launch_stream(const SkinnyArgs& a, const Levels& lv, const W4Plan& p,
     WQ_STR(47, 8, 1, 2, 1, 2)
     WQ_STR(50, 8, 2, 1, 16, 2)
     WQ_STR(51, 8, 4, 1, 16, 2)
+    WQ_STR(54, 4, 1, 2, 16, 2)
     WQ_STR(74, 16, 1, 1, 1, 2)
     default: return hipErrorInvalidConfiguration;
   }
@@ -1306,7 +1309,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   struct SCfg { int id, nw, tpg, gpp, mp, nbuf; };
   static const SCfg scfgs[] = {{40, 8, 1, 1, 1, 2},  {42, 8, 1, 1, 4, 2},  {43, 8, 3, 1, 16, 2},
                                {45, 8, 1, 1, 16, 2}, {47, 8, 1, 2, 1, 2},  {50, 8, 2, 1, 16, 2},
-                               {51, 8, 4, 1, 16, 2}, {74, 16, 1, 1, 1, 2}};
+                               {51, 8, 4, 1, 16, 2}, {54, 4, 1, 2, 16, 2}, {74, 16, 1, 1, 1, 2}};
   W4Plan p;
   p.path = m > 16 ? 1 : 3;
   p.tpg = 1;
@@ -1338,7 +1341,11 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
   //         A/B on one box, twice; NF4 and larger grids measured slower);
   //  m <= 4: eight waves, one tile;
   //  m <= 16: one workgroup per CU, as many tiles per workgroup as that
-  //           takes (at most 4; more tiles take several rounds).
+  //           takes (at most 4; more tiles take several rounds); INT4 with
+  //           one tile and K of 64 groups or more: four waves taking their
+  //           groups in pairs (whole-line code loads: 4096x11008 at m = 16
+  //           11.6 against 11.9 us; at K = 4096 6.1 against 5.9, so not
+  //           there).
   int cfg;
   if (m <= 1) {
     cfg = G >= 64 ? 47 : (w->fmt == WQ_FMT_INT4_ASYM && ntiles <= 256 ? 74 : 40);
@@ -1346,7 +1353,7 @@ W4Plan plan_w4a16(int64_t m, const wq_weight* w) {
     cfg = 42;
   } else {
     const int64_t tpg = (ntiles + 255) / 256;
-    cfg = tpg >= 4 ? 51 : tpg == 3 ? 43 : (tpg == 2 ? 50 : 45);
+    cfg = tpg >= 4 ? 51 : tpg == 3 ? 43 : (tpg == 2 ? 50 : (G >= 64 && w->fmt == WQ_FMT_INT4_ASYM ? 54 : 45));
   }
   for (const SCfg& sc : scfgs)
     if (sc.id == cfg) {

@@ -127,6 +127,8 @@ def oracle_linear(x_np, w_np, xdt, rows=None, group=128):
     (2, 300, 11008, "f16", "f16"),    # four staged rows, three phases
     (7, 200, 13824, "f16", "f32"),    # 108 groups: many phases per wave
     (16, 96, 5120, "bf16", "f32"),    # double-buffered phases, exact bf16 dequant
+    (8, 1000, 11008, "bf16", "bf16"), # 86 groups, one tile: four waves, whole-line code loads
+    (1, 300, 11008, "bf16", "f32"),   # m = 1, groups in pairs (whole lines), ragged n
 ])
 def test_linear_skinny_parity(m, n, k, xdt, ydt):
     say(f"linear_skinny m={m} n={n} k={k} x={xdt} y={ydt}")

@@ -813,7 +813,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a, Levels lv) {
 }
 
 // INT4 weights x fp16 activations GEMM (m > 16, prefill).  Workgroup tile
-// 128 (m) x 256 (n), NWG waves side by side along n (8: each 128 x 32 =
+// 128 (m) x 32 NWG (n), NWG waves side by side along n (8: each 128 x 32 =
 // 8 x 2 MFMA tiles of 16x16, two waves per SIMD); K advances one group (128)
 // per step.  Every code is
 // dequantized in registers by the wave that uses it, so the vector work per
@@ -854,12 +854,13 @@ template <int FMT, int XDT, int YDT, int NWG, int SUB>   // SUB: INT4 groups per
 __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv) {
   constexpr bool FAST = FMT == WQ_FMT_INT4_ASYM && XDT == WQ_F16;
   static_assert(FMT == WQ_FMT_INT4_ASYM || SUB == 1, "NF4 blocks: one unit of 128 = two blocks");
-  constexpr int NW = NWG, BM = 128, BN = 256;
+  constexpr int NW = NWG, BM = 128, BN = 32 * NWG;   // 32 code rows per wave
   constexpr int NF = BN / 16 / NW;               // 16-row code tiles per wave (n)
   constexpr int MI = BM / 16;                    // 16-row activation tiles per wave (m): all
   constexpr int XBUF = BM * 16;                  // 16-byte chunks per activation buffer
   constexpr int WBUF = BN * 4;                   // 16-byte chunks per code buffer
-  constexpr int XI = XBUF / 64 / NW;             // activation loads per wave and group
+  constexpr int XL = XBUF / 64;                  // activation loads per group
+  constexpr int XI = (XL + NW - 1) / NW;         // ... per wave, at most (fewer for some if NW does not divide XL)
   constexpr int WI = WBUF / 64 / NW;             // code loads per wave and group
   __shared__ uint4_t xr[2 * XBUF];
   __shared__ uint4_t wr[3 * WBUF];
@@ -938,7 +939,7 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv
   uint32_t xoff[XI], woff[WI];
 #pragma unroll
   for (int t = 0; t < XI; ++t) {
-    const int i = t * NW + wave;                 // load i fills slots 64 i .. 64 i + 63
+    const int i = min(t * NW + wave, XL - 1);    // load i fills slots 64 i .. 64 i + 63
     const int r = i * 4 + (lane >> 4);
     const int c16 = (lane & 15) ^ (r & 15);
     xoff[t] = (uint32_t)min(r, a.m - 1 - m0) * (uint32_t)(a.k * 2) + c16 * 16;
@@ -956,7 +957,9 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv
     const char* base = xb + (int64_t)min(gi, G - 1) * 256;
     uint4_t* buf = xr + (gi & 1) * XBUF;
 #pragma unroll
-    for (int t = 0; t < XI; ++t) lds_dma16(base + xoff[t], (lds_void_t*)(buf + (t * NW + wave) * 64));
+    for (int t = 0; t < XI; ++t)
+      if (XL % NW == 0 || t * NW + wave < XL)
+        lds_dma16(base + xoff[t], (lds_void_t*)(buf + (t * NW + wave) * 64));
   };
   auto issue_w = [&](int gi) {
     const char* base = cb + (int64_t)min(gi, G - 1) * 64;
@@ -1085,11 +1088,11 @@ __global__ __launch_bounds__(NWG * 64) void gemm_i4_kernel(GemmArgs a, Levels lv
       }
 }
 
-template <int FMT, int XDT, int YDT>
-hipError_t launch_gemm_i4(const GemmArgs& a, const Levels& lv, hipStream_t s) {
-  constexpr int NWG = kGemmWaves;
+template <int FMT, int XDT, int YDT, int NWG>
+hipError_t launch_gemm_i4_w(const GemmArgs& a, const Levels& lv, hipStream_t s) {
   // one launch per slice of rows keeps the 1-D grid within 2^22 workgroups
-  const int64_t ntn = (a.n + 255) / 256, ysz = YDT == WQ_F32 ? 4 : 2;
+  constexpr int BN = 32 * NWG;
+  const int64_t ntn = (a.n + BN - 1) / BN, ysz = YDT == WQ_F32 ? 4 : 2;
   const int64_t rows = 128 * std::max<int64_t>(1, (int64_t(1) << 22) / ntn);
   for (int64_t r0 = 0; r0 < a.m; r0 += rows) {
     GemmArgs b = a;
@@ -1111,6 +1114,20 @@ hipError_t launch_gemm_i4(const GemmArgs& a, const Levels& lv, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Eight waves (tiles 128 x 256) or seven (128 x 224): seven where the
+// narrower tiles need no more rounds of 256 workgroups, which shortens each
+// round by an eighth (the NF4 8B layer at m = 512: 256 tiles of 224 columns
+// in one round instead of 224 tiles of 256 on 224 CUs, 77.7 against
+// 96.0 us, the same bits, A/B in one run, twice).
+template <int FMT, int XDT, int YDT>
+hipError_t launch_gemm_i4(const GemmArgs& a, const Levels& lv, hipStream_t s) {
+  const int64_t ntm = (a.m + 127) / 128;
+  const int64_t r8 = ((a.n + 255) / 256 * ntm + 255) / 256;
+  const int64_t r7 = ((a.n + 223) / 224 * ntm + 255) / 256;
+  if (r7 * 224 < r8 * 256) return launch_gemm_i4_w<FMT, XDT, YDT, 7>(a, lv, s);
+  return launch_gemm_i4_w<FMT, XDT, YDT, kGemmWaves>(a, lv, s);
 }
 
 // INT4 groups per row (k / group); other formats: the units of 128.

@@ -127,6 +127,23 @@ def test_linear_nf4_full_layer(record_margin):
                       rel)
 
 
+@pytest.mark.parametrize("m,n,k", [(2048, 11008, 1024), (2048, 4296, 1024)])
+def test_linear_nf4_wide_prefill(m, n, k):
+    """NF4 prefill at M = 2048 over 11008 columns (three rounds of 256-wide
+    tiles) and 4296 columns (seven-wave 224-wide tiles: 320 against 272
+    tiles, both two rounds); 24 sampled rows, the last among them, against
+    the oracle, every column."""
+    say(f"linear_nf4_wide m={m} n={n} k={k}")
+    seed = 900 + n
+    x, _ = workloads.activations(m, k, seed, 0, dtype="bf16")
+    w = workloads.weights(n, k, seed, 1, dtype="bf16")
+    y, _ = run(x, w, "bf16", "bf16", True)
+    rows = np.random.default_rng(n).choice(m, 24, replace=False)
+    rows[0] = m - 1
+    rel = check_close(y[rows], oracle_y(x, w, "bf16", True, rows), "bf16")
+    say(f"  max-rel {rel:.2e}")
+
+
 # ---------------------------------------------------------------- FP4 (E2M1)
 
 def gpu_pack_fp4(w_dev, double_quant=True):

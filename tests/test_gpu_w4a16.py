@@ -318,6 +318,26 @@ def test_gate_up_group_sizes(m, n, k, group, act):
         check_close(to_np(yg), linear.silu_gated(g, u), "f32")
 
 
+@pytest.mark.parametrize("xdt,ydt,group", [("bf16", "bf16", 128), ("f16", "f16", 64),
+                                           ("f16", "f32", 32)])
+def test_gemm_up_shape(xdt, ydt, group):
+    """The up-projection width at M = 2048 (688 tiles of 128 x 256, three
+    rounds of 256 workgroups, the last one partly filled) with the exact bf16
+    decoder and groups of 64 and 32; 24 sampled rows, the last among them,
+    against the oracle, every column."""
+    m, n, k = 2048, 11008, 1024
+    say(f"gemm_up_shape m={m} n={n} k={k} x={xdt} y={ydt} group={group}")
+    seed = 800 + group
+    x, _ = workloads.activations(m, k, seed, 0, dtype=xdt)
+    w = workloads.weights(n, k, seed, 1, dtype=xdt)
+    qw = gpu_quantize_int4(dev(w, xdt), group)
+    y, _ = run_linear(x, w, xdt, ydt, qw=qw)
+    rows = np.random.default_rng(seed).choice(m, 24, replace=False)
+    rows[0] = m - 1
+    rel = check_close(y[rows], oracle_linear(x, w, xdt, rows=rows, group=group), ydt)
+    say(f"  max-rel {rel:.2e}")
+
+
 def _act_order_perm(k, seed):
     """A synthetic act-order: channels by decreasing seeded importance."""
     return np.argsort(-np.random.default_rng(seed).random(k), kind="stable").astype(np.int32)

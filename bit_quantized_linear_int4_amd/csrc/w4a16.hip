@@ -263,8 +263,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(SkinnyArgs a, Levels lv
   // M = 1 the ring is faster, 13.1 against 14.1 us; A/B in one run)
   constexpr bool CRING = SZL && (!DUAL || MP == 1);
   // whole-line code loads (codes through the LDS ring, groups taken in
-  // pairs): a load covers 8 rows x 128 bytes, two adjacent groups, instead of 16 rows x 64
-  // bytes, so no 128-byte line is split between two loads; lane l of load v
+  // pairs): a load covers 8 rows x 128 bytes, two adjacent groups, instead
+  // of 16 rows x 64 bytes, so no 128-byte line is split between two loads;
+  // lane l of load v
   // of a pair brings chunk (l & 7) ^ lsw(r) of row r = 8 v + (l >> 3), which
   // keeps the 16 rows an operand read gathers in different LDS banks
   // (4096 x 11008 at M = 1: 8.06-8.18 against 8.41-8.46 us, the same bits;
@@ -1450,16 +1451,17 @@ W4Plan plan_w4a16_pair(int64_t m, const wq_weight* wg, const wq_weight* wu) {
 namespace {
 
 // yg = silu(yg) * yu elementwise, in fp32 on the stored values (the SiLU
-// product after the two prefill GEMMs); 8 elements per lane, the tail
-// element by element.
+// product after the two prefill GEMMs); a workgroup takes 2048 consecutive
+// elements, lane l the elements l, l + 256, ... of them, so every load and
+// store of a wave covers consecutive elements.
 template <int YDT>
 __global__ __launch_bounds__(256) void silu_mul_kernel(void* __restrict__ yg,
                                                        const void* __restrict__ yu,
                                                        int64_t count) {
-  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int64_t i0 = (int64_t)blockIdx.x * 2048 + threadIdx.x;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t i = i0 + j;
+    const int64_t i = i0 + j * 256;
     if (i >= count) return;
     float g, u;
     if constexpr (YDT == WQ_F32) {
